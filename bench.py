@@ -1,0 +1,199 @@
+"""Learner-head benchmark: one step = rz_logprob -> rz_is_loss -> rz_d3 ->
+rz_backward over one synthetic batch resident in HBM.
+
+    python bench.py [--steps K] [--warmup W] [--config qwen15b]
+
+Prints ONE JSON line.  `value` is learner tokens per second on one GPU;
+`roofline` covers the LM-head forward kernel (timed live with HIP events on
+the stream it runs on); `cpu_baseline` times the float64 oracle on a bounded
+sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BYTES = 8.0e12
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = [
+    os.path.join(ROOT, "invariant_logprob_is_amd", "csrc", f)
+    for f in ("rz_kernels.hip", "rz_gemm.h", "rz_internal.h")
+]
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def source_sha() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when it is missing or was taken on different kernel sources."""
+    p = os.path.join(PROFILES, f"traffic_{kernel}.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("source_sha") != source_sha():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def cpu_baseline(b, n_tokens: int):
+    """The oracle as it stands, on the first `n_tokens` rows of the batch
+    (whole responses are not needed: rows are independent in the head)."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    n = min(n_tokens, b.T)
+    rows = slice(0, n)
+    mu_noise = b.lag_noise[rows].astype(np.float64)
+    t0 = time.perf_counter()
+    lp, lse = oracle.logprob(b.x[rows], b.gamma, b.eps, b.W, b.target[rows])
+    mu = lp + mu_noise
+    ro = np.array([0, n], np.int64)
+    go = np.array([0, 1], np.int64)
+    L = oracle.is_loss(lp, mu, ro, go, b.reward[:1])
+    oracle.d3(lp, mu)
+    oracle.backward(b.x[rows], b.gamma, b.eps, b.W, b.target[rows], lse, L["coef"])
+    dt = time.perf_counter() - t0
+    return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"first {n} rows of the workload: RMSNorm, LM head, log-softmax, IS loss, "
+                      f"D3 and backward to the hidden states in float64 numpy ({dt:.1f} s)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="qwen15b",
+                    choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
+    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import torch
+    import invariant_logprob_is_amd as rz
+    import workloads
+
+    rz.lib()
+    dev = torch.device("cuda", 0)
+    t_gen = time.perf_counter()
+    b = workloads.CONFIGS[args.config]()
+    log(f"generated {args.config}: T={b.T} H={b.H} V={b.V} R={b.R} G={b.G} "
+        f"in {time.perf_counter() - t_gen:.1f}s")
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    x, g, W = bf16(b.x), bf16(b.gamma), bf16(b.W)
+    tgt = torch.from_numpy(b.target).to(dev)
+    ro = torch.from_numpy(b.resp_offsets).to(dev)
+    go = torch.from_numpy(b.group_offsets).to(dev)
+    reward = torch.from_numpy(b.reward).to(dev)
+    rz.validate_offsets(b.resp_offsets, b.group_offsets, b.T)
+    ws = torch.empty(rz.workspace_bytes(b.T, b.H, b.V), dtype=torch.uint8, device=dev)
+    lp = torch.empty(b.T, dtype=torch.float32, device=dev)
+    lse = torch.empty(b.T, dtype=torch.float32, device=dev)
+    dh = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
+    log(f"workspace {ws.numel() / 2**30:.2f} GiB")
+
+    # Rollout log-probabilities: the learner log-probability plus lag noise
+    # (a setup step, outside the timed region).
+    rz.logprob(x, g, W, tgt, b.eps, workspace=ws, out=lp, lse_out=lse)
+    mu = (lp + torch.from_numpy(b.lag_noise).to(dev)).contiguous()
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream(dev)
+
+    def step(evs=None):
+        if evs is not None:
+            evs[0].record(stream)
+        rz.logprob(x, g, W, tgt, b.eps, workspace=ws, out=lp, lse_out=lse)
+        if evs is not None:
+            evs[1].record(stream)
+        loss, coef, _ = rz.is_loss(lp, mu, ro, go, reward, workspace=ws, want_advantage=False)
+        d3 = rz.d3(lp, mu, workspace=ws)
+        if evs is not None:
+            evs[2].record(stream)
+        rz.backward(x, g, W, tgt, lse, coef, b.eps, workspace=ws, out=dh)
+        if evs is not None:
+            evs[3].record(stream)
+        return loss, d3
+
+    for i in range(args.warmup):
+        step()
+        log(f"warmup {i + 1}/{args.warmup}")
+    torch.cuda.synchronize()
+
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        loss, d3 = step(evs[i])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = 1000.0 * wall / args.steps
+    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
+    loss_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
+    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
+    log(f"step {ms_step:.2f} ms (logprob {fwd_ms:.2f}, loss+d3 {loss_ms:.3f}, backward {bwd_ms:.2f}); "
+        f"loss={loss.item():.6e} d3={d3.item():.6e}")
+
+    T, H, V = b.T, b.H, b.V
+    tokens_per_s = T / (ms_step / 1000.0)
+    alg_flops_token = 4.0 * H * V
+    fwd_flops = 2.0 * T * H * V          # algorithmic flops of one LM-head forward launch
+    achieved = fwd_flops / (fwd_ms / 1000.0)
+    roofline = {
+        "kernel": "k_lmhead_fwd (LM head + online log-sum-exp; event interval spans the whole "
+                  "rz_logprob call)",
+        "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
+        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS,
+        "traffic": measured_traffic("k_lmhead_fwd"),
+    }
+    out = {
+        "metric": "learner tokens/sec (fwd+bwd logprob+IS loss) and % bf16 MFMA peak, 1 GPU",
+        "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}, {b.R} responses in {b.G} groups",
+                   "T": T, "H": H, "V": V, "R": b.R, "G": b.G},
+        "mfma_frac_algorithmic": tokens_per_s * alg_flops_token / PEAK_BF16_FLOPS,
+        "stage_ms": {"logprob": fwd_ms, "is_loss_d3": loss_ms, "backward": bwd_ms},
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log(f"cpu baseline on {args.cpu_tokens} tokens ...")
+        out["cpu_baseline"] = cpu_baseline(b, args.cpu_tokens)
+        log(f"cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s")
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

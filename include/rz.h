@@ -1,0 +1,175 @@
+/*
+ * rz.h -- C ABI of the REINFORCE Zero learner head for AMD MI355X (gfx950).
+ *
+ * The library computes, for a ragged batch of response tokens:
+ *   - per-token log-probabilities of the sampled tokens whose bits do not
+ *     depend on how the batch is composed (batch size, a row's offset, a
+ *     single-row call versus a large one);
+ *   - the unclipped token-level importance-sampled REINFORCE loss and its
+ *     gradient with respect to each log-probability;
+ *   - the D3 diagnostic;
+ *   - the gradient of the loss with respect to the pre-norm hidden states.
+ *
+ * Sources (web pages describing the method):
+ *   [P1] "REINFORCE-Zero: kernel alignment + unclipped IS enables 20K-step
+ *        stable async RL", sections "Core insight" and "Results".
+ *   [P2] "Zero Mismatch, Simple Async RL: REINFORCE Zero, DeepSeek-V4.1 and
+ *        Kimi K3.1", sections "Only one probability gap comes from old
+ *        weights" (the log-ratio decomposition equation), "Alignment permits a
+ *        simpler learning path", "Large-model validation exposes concrete
+ *        failure mechanisms".
+ *   [P3] "REINFORCE Zero：为什么内核对齐后，极简 IS 能让异步 RL 稳定训练 20,000 步？",
+ *        body text and the captions of Fig. 1 and Fig. 2.
+ *
+ * Conventions for every entry point:
+ *   - Memory: every array pointer is a caller-owned DEVICE pointer on the
+ *     current HIP device.  The library never allocates or frees memory; all
+ *     scratch comes from the caller's `workspace` (device memory, 256-byte
+ *     aligned, at least rz_workspace_bytes(T, H, V) bytes).
+ *   - bf16 arrays are passed as uint16_t storage bits.
+ *   - Streams: `stream` is a hipStream_t (NULL = the null stream).  Calls
+ *     enqueue their kernels and return without synchronising; outputs are
+ *     valid once the stream reaches that point.  Calls on one workspace must
+ *     be ordered (same stream or explicit events).
+ *   - Validation: every check that needs no device data runs on the host
+ *     before any HIP call, so argument errors are reported on machines
+ *     without a GPU.  Data that lives on the device (targets, offsets) is
+ *     not inspected on the host: an out-of-range target yields NaN for that
+ *     token's log-probability, and malformed offsets yield a NaN loss.
+ *   - Determinism: no atomics; outputs are bitwise identical run to run.
+ *   - Layout: row t pairs the final hidden state that predicts target[t] with
+ *     that target (the caller applies the next-token shift and drops prompt
+ *     tokens).  Tokens of a response are contiguous; the responses of one
+ *     prompt group are contiguous.
+ *   - Thread safety: no global mutable state; concurrent calls are safe if
+ *     they use distinct workspaces and outputs.
+ */
+#ifndef RZ_H_
+#define RZ_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define RZ_OK 0
+#define RZ_EINVAL 1        /* null/misaligned pointer, negative or zero size   */
+#define RZ_EUNSUPPORTED 2  /* valid but unsupported shape (see each call)      */
+#define RZ_ENODEV 3        /* no HIP device available                          */
+#define RZ_EHIP 4          /* a HIP runtime call or kernel launch failed       */
+#define RZ_EWORKSPACE 5    /* workspace smaller than rz_workspace_bytes()      */
+
+/* Library version, (major << 16) | (minor << 8) | patch. */
+int rz_version(void);
+
+/* Static, human-readable text for a status code. */
+const char* rz_status_string(int status);
+
+/* Workspace size (bytes) that suffices for every entry point below at these
+ * sizes.  Returns 0 if the sizes are invalid.  Host only, no HIP call. */
+size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
+
+/*
+ * rz_logprob -- batch-invariant learner log-probabilities.
+ *
+ * Computes, for every row t < T:
+ *   hhat_t   = bf16_rne(gamma * x_t * (mean_k x_tk^2 + eps)^(-1/2))
+ *   z_tv     = sum_k hhat_tk W_vk          (bf16 MFMA, fp32 accumulation)
+ *   lse[t]   = log sum_v exp(z_tv)
+ *   logprob[t] = z_{t, target[t]} - lse[t]
+ * This is the learner's log pi(y_t | history) of [P2] "Only one probability
+ * gap comes from old weights"; its bits must not depend on batch composition
+ * so that the kernel-mismatch term of the decomposition is exactly zero
+ * ([P2] "Alignment permits a simpler learning path"; [P3] body).
+ *
+ * Invariance: the bits of logprob[t] and lse[t] depend only on x_t, gamma,
+ * eps, W and target[t]: not on T, on t, or on the other rows.  Tile shapes
+ * and the vocabulary reduction order depend on (H, V) only.
+ *
+ * x [T,H] bf16 row-major; gamma [H] bf16; W [V,H] bf16 row-major; target [T]
+ * int32 in [0, V) (out of range -> NaN logprob); logprob [T] fp32 out;
+ * lse [T] fp32 out, may be NULL.  All pointers 16-byte aligned.
+ * Errors: RZ_EINVAL (null pointer, T < 1, H < 1, V < 1, misalignment),
+ * RZ_EUNSUPPORTED (H not a multiple of 64, H > 16384, V > 2^23),
+ * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
+ */
+int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
+               const uint16_t* W, const int32_t* target,
+               int64_t T, int32_t H, int32_t V,
+               float* logprob, float* lse,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_is_loss -- unclipped token-level IS REINFORCE loss and its gradient.
+ *
+ * ([P2] "Alignment permits a simpler learning path": advantage = reward minus
+ *  the group mean, tokens averaged within each response, no value model, no
+ *  rejection gate; [P1] lede and [P3] body: unclipped token-level IS with
+ *  w = exp(log pi - log mu).)
+ *   A_i     = reward[i] - mean_{j in group(i)} reward[j]
+ *   w_t     = exp(logprob[t] - rollout_logprob[t])            (no clip)
+ *   loss    = -(1/R) sum_i A_i (1/L_i) sum_{t in i} w_t
+ *   coef[t] = d loss / d logprob[t] = -A_i w_t / (R L_i)
+ * Sums are accumulated in fp64 in a fixed order.
+ *
+ * logprob, rollout_logprob [T] fp32; resp_offsets [R+1] int64 token offsets
+ * (resp_offsets[0] = 0, resp_offsets[R] = T, strictly increasing);
+ * group_offsets [G+1] int64 response offsets of the prompt groups
+ * (group_offsets[0] = 0, group_offsets[G] = R, strictly increasing);
+ * reward [R] fp32.  Outputs: loss [1] fp64; coef [T] fp32 (may be NULL);
+ * advantage [R] fp32 (may be NULL).  Offsets are read on the device: a
+ * malformed structure writes NaN to loss (and to the coef of the affected
+ * responses); no out-of-bounds access happens.
+ * Errors: RZ_EINVAL (null pointer, T < 1, R < 1, G < 1, R > T, G > R),
+ * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
+ */
+int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
+               const int64_t* resp_offsets, int32_t R,
+               const int64_t* group_offsets, int32_t G,
+               const float* reward,
+               double* loss, float* coef, float* advantage,
+               void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_d3 -- the D3 diagnostic ([P2] "Only one probability gap comes from old
+ * weights": the per-update token mean of w - 1 - log w; [P3] Fig. 2 caption:
+ * a batch average).  With delta = logprob - rollout_logprob,
+ *   d3 = (1/T) sum_t (expm1(delta_t) - delta_t),   fp64, fixed order.
+ * Output d3 [1] fp64.
+ * Errors: RZ_EINVAL (null pointer, T < 1), RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
+ */
+int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
+          double* d3, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_backward -- gradient of the loss with respect to the pre-norm hidden
+ * states, given lse (from rz_logprob) and coef (from rz_is_loss).
+ *
+ * With p_tv = exp(z_tv - lse_t), the logit gradient is coef_t (onehot - p)
+ * and
+ *   dhhat_t = coef_t * (W[target_t] - sum_v p_tv W_v)
+ * (the one-hot term is gathered exactly in fp32; P is rounded to bf16 and
+ * contracted on bf16 MFMA with fp32 accumulation in a fixed vocabulary
+ * order), followed by the RMSNorm backward in fp64/fp32, the bf16 rounding
+ * of hhat being treated as the identity:
+ *   dx_j = r gamma_j g_j - x_j r^3 (1/H) sum_k gamma_k g_k x_k.
+ *
+ * x, gamma, eps, W, target as for rz_logprob; lse, coef [T] fp32;
+ * dhidden [T,H] fp32 out.
+ * Errors: as rz_logprob.
+ */
+int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
+                const uint16_t* W, const int32_t* target,
+                const float* lse, const float* coef,
+                int64_t T, int32_t H, int32_t V,
+                float* dhidden,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}  /* extern "C" */
+#endif
+
+#endif  /* RZ_H_ */

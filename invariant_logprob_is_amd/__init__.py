@@ -1,0 +1,248 @@
+"""Python binding of librz.so, the HIP library declared in include/rz.h.
+
+Argument marshalling only: every step of the learner head runs in the HIP
+kernels behind the C ABI.  PyTorch supplies device memory and the current
+stream.  There is no CPU fallback: if librz.so is missing, every call raises.
+
+    import invariant_logprob_is_amd as rz
+    lp, lse = rz.logprob(x, gamma, W, target)             # batch-invariant
+    loss, coef, adv = rz.is_loss(lp, mu, resp_offsets, group_offsets, reward)
+    d3 = rz.d3(lp, mu)
+    dx = rz.backward(x, gamma, W, target, lse, coef)
+
+bf16 tensors are torch.bfloat16; log-probabilities fp32; offsets int64.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "RzError", "lib", "version", "workspace_bytes", "logprob", "is_loss", "d3",
+    "backward", "LIB_PATH", "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
+    "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librz.so")
+
+RZ_OK, RZ_EINVAL, RZ_EUNSUPPORTED, RZ_ENODEV, RZ_EHIP, RZ_EWORKSPACE = range(6)
+
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_I32 = ctypes.c_int32
+_F32 = ctypes.c_float
+_SZ = ctypes.c_size_t
+
+# name -> (restype, argtypes); mirrors include/rz.h
+SYMBOLS = {
+    "rz_version": (ctypes.c_int, []),
+    "rz_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "rz_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "rz_logprob": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
+    "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "rz_backward": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+}
+
+_lib = None
+
+
+class RzError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().rz_status_string(status).decode() if _lib is not None else str(status)
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+
+
+def lib() -> ctypes.CDLL:
+    """Load librz.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m invariant_logprob_is_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SYMBOLS.items():
+            f = getattr(L, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = L
+    return _lib
+
+
+def version() -> int:
+    return lib().rz_version()
+
+
+def workspace_bytes(T: int, H: int, V: int) -> int:
+    return int(lib().rz_workspace_bytes(T, H, V))
+
+
+def _check(fn: str, status: int):
+    if status != RZ_OK:
+        raise RzError(fn, status)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(device) -> int:
+    torch = _torch()
+    return int(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, device, ndim=None):
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name}: expected a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name}: expected {ndim} dims, got {t.dim()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name}: must be contiguous")
+    return t
+
+
+def _workspace(nbytes: int, device, workspace):
+    torch = _torch()
+    if workspace is None:
+        return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    if workspace.numel() < nbytes:
+        raise ValueError(f"workspace too small: {workspace.numel()} < {nbytes} bytes")
+    return workspace
+
+
+def logprob(x, gamma, W, target, eps: float = 1e-6, *, workspace=None, out=None,
+            lse_out=None):
+    """Batch-invariant per-token log-probabilities (rz_logprob).
+
+    x [T,H] bf16, gamma [H] bf16, W [V,H] bf16, target [T] int32, all on one
+    GPU.  Returns (logprob [T] fp32, lse [T] fp32)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    V = W.shape[0]
+    if gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T:
+        raise ValueError("shape mismatch among x, gamma, W, target")
+    lp = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    ls = lse_out if lse_out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    _need(lp, "out", torch.float32, dev, 1)
+    _need(ls, "lse_out", torch.float32, dev, 1)
+    nb = workspace_bytes(T, H, V)
+    ws = _workspace(nb, dev, workspace)
+    st = lib().rz_logprob(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                          target.data_ptr(), T, H, V, lp.data_ptr(), ls.data_ptr(),
+                          ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_logprob", st)
+    return lp, ls
+
+
+def validate_offsets(resp_offsets, group_offsets, T: int):
+    """Host-side check of the ragged structure (the library itself can only
+    detect malformed device offsets as a NaN loss)."""
+    import numpy as np
+    ro = np.asarray(resp_offsets, dtype=np.int64)
+    go = np.asarray(group_offsets, dtype=np.int64)
+    R, G = len(ro) - 1, len(go) - 1
+    if R < 1 or G < 1:
+        raise ValueError("need at least one response and one group")
+    if ro[0] != 0 or ro[-1] != T or np.any(np.diff(ro) <= 0):
+        raise ValueError("resp_offsets must start at 0, end at T and strictly increase")
+    if go[0] != 0 or go[-1] != R or np.any(np.diff(go) <= 0):
+        raise ValueError("group_offsets must start at 0, end at R and strictly increase")
+
+
+def _offsets_on(t, dev, name):
+    torch = _torch()
+    t = torch.as_tensor(t, dtype=torch.int64)
+    if t.device != dev:
+        t = t.to(dev)
+    return _need(t.contiguous(), name, torch.int64, dev, 1)
+
+
+def is_loss(logprob, rollout_logprob, resp_offsets, group_offsets, reward, *,
+            workspace=None, want_coef: bool = True, want_advantage: bool = True):
+    """Unclipped token-level IS REINFORCE loss (rz_is_loss).
+
+    Offsets given on the host are validated there first.  Returns
+    (loss [1] fp64, coef [T] fp32 or None, advantage [R] fp32 or None)."""
+    torch = _torch()
+    dev = logprob.device
+    _need(logprob, "logprob", torch.float32, dev, 1)
+    _need(rollout_logprob, "rollout_logprob", torch.float32, dev, 1)
+    T = logprob.shape[0]
+    if rollout_logprob.shape[0] != T:
+        raise ValueError("logprob and rollout_logprob differ in length")
+    if not (isinstance(resp_offsets, torch.Tensor) and resp_offsets.is_cuda):
+        validate_offsets(resp_offsets, group_offsets, T)
+    ro = _offsets_on(resp_offsets, dev, "resp_offsets")
+    go = _offsets_on(group_offsets, dev, "group_offsets")
+    R, G = ro.shape[0] - 1, go.shape[0] - 1
+    rw = _need(torch.as_tensor(reward, dtype=torch.float32).to(dev).contiguous(), "reward",
+               torch.float32, dev, 1)
+    if rw.shape[0] != R:
+        raise ValueError("reward must have one entry per response")
+    loss = torch.empty(1, dtype=torch.float64, device=dev)
+    coef = torch.empty(T, dtype=torch.float32, device=dev) if want_coef else None
+    adv = torch.empty(R, dtype=torch.float32, device=dev) if want_advantage else None
+    ws = _workspace(workspace_bytes(T, 64, 1), dev, workspace)
+    st = lib().rz_is_loss(logprob.data_ptr(), rollout_logprob.data_ptr(), T, ro.data_ptr(), R,
+                          go.data_ptr(), G, rw.data_ptr(), loss.data_ptr(),
+                          coef.data_ptr() if coef is not None else None,
+                          adv.data_ptr() if adv is not None else None,
+                          ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_is_loss", st)
+    return loss, coef, adv
+
+
+def d3(logprob, rollout_logprob, *, workspace=None):
+    """D3 diagnostic (rz_d3): token mean of w - 1 - log w.  Returns [1] fp64."""
+    torch = _torch()
+    dev = logprob.device
+    _need(logprob, "logprob", torch.float32, dev, 1)
+    _need(rollout_logprob, "rollout_logprob", torch.float32, dev, 1)
+    T = logprob.shape[0]
+    if rollout_logprob.shape[0] != T:
+        raise ValueError("logprob and rollout_logprob differ in length")
+    out = torch.empty(1, dtype=torch.float64, device=dev)
+    ws = _workspace(workspace_bytes(T, 64, 1), dev, workspace)
+    st = lib().rz_d3(logprob.data_ptr(), rollout_logprob.data_ptr(), T, out.data_ptr(),
+                     ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_d3", st)
+    return out
+
+
+def backward(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, workspace=None, out=None):
+    """Gradient of the loss with respect to the pre-norm hidden states
+    (rz_backward).  Returns dhidden [T,H] fp32."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    _need(lse, "lse", torch.float32, dev, 1)
+    _need(coef, "coef", torch.float32, dev, 1)
+    V = W.shape[0]
+    if (gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T or lse.shape[0] != T
+            or coef.shape[0] != T):
+        raise ValueError("shape mismatch among backward arguments")
+    dh = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=dev)
+    _need(dh, "out", torch.float32, dev, 2)
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    st = lib().rz_backward(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                           target.data_ptr(), lse.data_ptr(), coef.data_ptr(), T, H, V,
+                           dh.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_backward", st)
+    return dh

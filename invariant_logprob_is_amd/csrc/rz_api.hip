@@ -1,0 +1,156 @@
+// C ABI of the learner head (declared in include/rz.h).  Every check that
+// needs no device data runs before the first HIP call.
+#include "rz.h"
+#include "rz_internal.h"
+
+namespace {
+
+using namespace rz;
+
+constexpr int kVersion = (0 << 16) | (1 << 8) | 0;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned8(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 7u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int check_device() {
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || n <= 0) {
+    (void)hipGetLastError();
+    return RZ_ENODEV;
+  }
+  return RZ_OK;
+}
+
+int status_of(hipError_t e) { return e == hipSuccess ? RZ_OK : RZ_EHIP; }
+
+// Shape checks shared by rz_logprob and rz_backward.
+int check_head_shape(int64_t T, int32_t H, int32_t V) {
+  if (T < 1 || H < 1 || V < 1) return RZ_EINVAL;
+  if (H % kHAlign != 0 || H > kMaxH || int64_t(V) > kMaxV) return RZ_EUNSUPPORTED;
+  return RZ_OK;
+}
+
+template <class T_>
+T_* at(void* ws, size_t off) {
+  return reinterpret_cast<T_*>(static_cast<char*>(ws) + off);
+}
+
+}  // namespace
+
+extern "C" {
+
+int rz_version(void) { return kVersion; }
+
+const char* rz_status_string(int status) {
+  switch (status) {
+    case RZ_OK: return "ok";
+    case RZ_EINVAL: return "invalid argument";
+    case RZ_EUNSUPPORTED: return "unsupported shape";
+    case RZ_ENODEV: return "no HIP device";
+    case RZ_EHIP: return "HIP runtime error";
+    case RZ_EWORKSPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V) {
+  if (T < 1 || H < 1 || V < 1) return 0;
+  return ws_layout(T, H, V).total;
+}
+
+int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+               const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
+               float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !gamma || !W || !target || !logprob || !workspace) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) ||
+      !aligned4(logprob) || (lse && !aligned4(lse)) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  const WsLayout L = ws_layout(T, H, V);
+  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* hhat = at<uint16_t>(workspace, L.hhat);
+  float* pm = at<float>(workspace, L.pm);
+  float* ps = at<float>(workspace, L.ps);
+  float* zt = at<float>(workspace, L.ztgt);
+  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
+  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, s);
+  if (e == hipSuccess) e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, s);
+  return status_of(e);
+}
+
+int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
+               const int64_t* resp_offsets, int32_t R, const int64_t* group_offsets, int32_t G,
+               const float* reward, double* loss, float* coef, float* advantage, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  if (!logprob || !rollout_logprob || !resp_offsets || !group_offsets || !reward || !loss ||
+      !workspace)
+    return RZ_EINVAL;
+  if (!aligned4(logprob) || !aligned4(rollout_logprob) || !aligned8(resp_offsets) ||
+      !aligned8(group_offsets) || !aligned4(reward) || !aligned8(loss) ||
+      (coef && !aligned4(coef)) || (advantage && !aligned4(advantage)) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (T < 1 || R < 1 || G < 1 || int64_t(R) > T || G > R) return RZ_EINVAL;
+  const WsLayout L = ws_layout(T, 64, 1);
+  if (workspace_bytes < L.loss_end) return RZ_EWORKSPACE;
+  const int st = check_device();
+  if (st != RZ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(launch_is_loss(logprob, rollout_logprob, T, resp_offsets, R, group_offsets, G,
+                                  reward, loss, coef, advantage, at<double>(workspace, L.part), s));
+}
+
+int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T, double* d3,
+          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logprob || !rollout_logprob || !d3 || !workspace) return RZ_EINVAL;
+  if (!aligned4(logprob) || !aligned4(rollout_logprob) || !aligned8(d3) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (T < 1) return RZ_EINVAL;
+  const WsLayout L = ws_layout(T, 64, 1);
+  if (workspace_bytes < L.loss_end) return RZ_EWORKSPACE;
+  const int st = check_device();
+  if (st != RZ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(launch_d3(logprob, rollout_logprob, T, d3, at<double>(workspace, L.part), s));
+}
+
+int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                const int32_t* target, const float* lse, const float* coef, int64_t T, int32_t H,
+                int32_t V, float* dhidden, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !gamma || !W || !target || !lse || !coef || !dhidden || !workspace) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) || !aligned4(lse) ||
+      !aligned4(coef) || !aligned16(dhidden) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  const WsLayout L = ws_layout(T, H, V);
+  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* hhat = at<uint16_t>(workspace, L.b_hhat);
+  uint16_t* Wt = at<uint16_t>(workspace, L.b_wt);
+  uint16_t* P = at<uint16_t>(workspace, L.b_p);
+  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
+  if (e == hipSuccess) e = launch_transpose_w(W, H, V, Wt, s);
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    e = launch_softmax_p(hhat + c0 * H, W, lse + c0, tc, H, V, P, s);
+    if (e == hipSuccess)
+      e = launch_dhidden(P, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
+  }
+  if (e == hipSuccess) e = launch_rmsnorm_bwd(x, gamma, eps, T, H, dhidden, s);
+  return status_of(e);
+}
+
+}  // extern "C"

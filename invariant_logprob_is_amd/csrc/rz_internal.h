@@ -1,0 +1,93 @@
+// Internal declarations shared by the kernel and ABI translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rz {
+
+// ---------------------------------------------------------------------------
+// Fixed tiling.  Every shape decision below depends on (H, V) only, never on
+// the token count T or on where a row sits in the batch.
+// ---------------------------------------------------------------------------
+constexpr int kTile = 256;          // operand rows per workgroup tile (both operands)
+constexpr int kBK = 64;             // K elements per pipeline stage
+constexpr int kHAlign = 64;         // H must be a multiple of this
+constexpr int kMaxH = 16384;
+constexpr int64_t kMaxV = int64_t(1) << 23;  // keeps 256 * padded V below 2^32
+constexpr int64_t kBwdChunk = 32768;  // tokens per backward chunk (bounds the P workspace)
+constexpr int kTokenGroup = 8;      // token tiles per L2 group in the tile raster
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
+inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
+
+inline int64_t n_vocab_tiles(int64_t V) { return ceil_div(V, kTile); }
+inline int64_t vocab_pad(int64_t V) { return round_up(V, kBK); }
+
+// Workspace layout; every region starts on a 256-byte boundary.  Regions of
+// different entry points overlap (calls on one workspace are ordered).
+struct WsLayout {
+  // rz_logprob
+  size_t hhat, pm, ps, ztgt, fwd_end;
+  // rz_backward
+  size_t b_hhat, b_wt, b_p, bwd_end;
+  // rz_is_loss / rz_d3
+  size_t part, loss_end;
+  size_t total;
+};
+
+inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
+  WsLayout L{};
+  const int64_t Tp = round_up(T, kTile);
+  const int64_t nvt = n_vocab_tiles(V);
+  const int64_t Vp = vocab_pad(V);
+  size_t o = 0;
+  L.hhat = o;  o = align256(o + size_t(Tp) * H * 2);
+  L.pm = o;    o = align256(o + size_t(nvt) * T * 4);
+  L.ps = o;    o = align256(o + size_t(nvt) * T * 4);
+  L.ztgt = o;  o = align256(o + size_t(T) * 4);
+  L.fwd_end = o;
+  o = 0;
+  L.b_hhat = o; o = align256(o + size_t(Tp) * H * 2);
+  L.b_wt = o;   o = align256(o + size_t(H) * Vp * 2);
+  const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
+  L.b_p = o;    o = align256(o + size_t(round_up(tc, kTile)) * Vp * 2);
+  L.bwd_end = o;
+  o = 0;
+  L.part = o;   o = align256(o + size_t(T + 1) * 8);
+  L.loss_end = o;
+  L.total = L.fwd_end;
+  if (L.bwd_end > L.total) L.total = L.bwd_end;
+  if (L.loss_end > L.total) L.total = L.loss_end;
+  return L;
+}
+
+// ---------------------------------------------------------------------------
+// Kernel launchers (rz_kernels.hip).  All enqueue on `s` and return the
+// launch status (hipGetLastError after the launches).
+// ---------------------------------------------------------------------------
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps,
+                              int64_t T, int H, uint16_t* hhat, hipStream_t s);
+hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
+                             int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
+                             hipStream_t s);
+hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt,
+                              int64_t T, int V, float* logprob, float* lse, hipStream_t s);
+hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s);
+hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
+                            int64_t TC, int H, int V, uint16_t* P, hipStream_t s);
+hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t* W,
+                          const int32_t* target_chunk, const float* coef_chunk,
+                          int64_t TC, int H, int V, float* dh_chunk, hipStream_t s);
+hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float eps,
+                              int64_t T, int H, float* dh, hipStream_t s);
+hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T,
+                          const int64_t* ro, int R, const int64_t* go, int G,
+                          const float* reward, double* loss, float* coef, float* adv,
+                          double* part, hipStream_t s);
+hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3,
+                     double* part, hipStream_t s);
+
+}  // namespace rz

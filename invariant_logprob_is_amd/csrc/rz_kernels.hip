@@ -1,0 +1,589 @@
+// HIP kernels of the learner head for gfx950.  Built with -ffp-contract=off so
+// that every fused multiply-add below is an explicit fmaf and the arithmetic a
+// row sees is exactly what is written.
+#include <math.h>
+
+#include "rz_gemm.h"
+
+namespace rz {
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(uint32_t(b) << 16);
+}
+
+// float64 -> bf16, round to nearest even, with a single rounding: round to
+// odd at float32 precision (24 bits, >= 8 + 2) and then to nearest even at
+// bf16 precision, which composes to the correctly rounded result.
+__device__ __forceinline__ uint16_t f64_to_bf16_rne(double d) {
+  const float f = float(d);
+  uint32_t u = __float_as_uint(f);
+  const double back = double(f);
+  if (back != d) {
+    if (fabs(back) > fabs(d)) u -= 1u;  // step the magnitude back toward zero
+    u |= 1u;                            // sticky bit: round to odd
+  }
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+// Sum over a 64-lane wavefront by xor butterfly.  At every level the two
+// partners add the same two values (a + b and b + a), so all lanes finish with
+// identical bits, and the tree does not depend on where the row sits in the
+// batch.
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, 64);
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// Final RMSNorm (forward), one 64-lane wave per row, float64 internally.
+//   ms = (1/H) sum_k x_k^2,  r = (ms + eps)^(-1/2),  hhat_k = bf16(gamma_k x_k r)
+// Each lane accumulates its strided 8-element chunks in a fixed order; the
+// wave then reduces with wave_sum.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double row_sumsq(const uint16_t* __restrict__ xr, int H, int lane) {
+  double ss = 0.0;
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double lo = double(__uint_as_float(v[q] << 16));
+      const double hi = double(__uint_as_float(v[q] & 0xFFFF0000u));
+      ss = fma(lo, lo, ss);
+      ss = fma(hi, hi, ss);
+    }
+  }
+  return wave_sum(ss);
+}
+
+__global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ gamma, float eps,
+                                                     int64_t T, int H, uint16_t* __restrict__ hhat) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint16_t* xr = x + t * H;
+  const double ss = row_sumsq(xr, H, lane);
+  const double r = 1.0 / sqrt(ss / double(H) + double(eps));
+  uint16_t* hr = hhat + t * H;
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
+    u32x4 o;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double xl = double(__uint_as_float(v[q] << 16));
+      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
+      const double gl = double(__uint_as_float(g[q] << 16));
+      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
+      const uint32_t yl = f64_to_bf16_rne((gl * xl) * r);
+      const uint32_t yh = f64_to_bf16_rne((gh * xh) * r);
+      o[q] = yl | (yh << 16);
+    }
+    *reinterpret_cast<u32x4*>(hr + c) = o;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// RMSNorm backward, in place on dh (fp32), one wave per row.
+//   dx_j = r gamma_j g_j - x_j r^3 (1/H) sum_k gamma_k g_k x_k
+// r is recomputed with the forward's exact code (row_sumsq), so it has the
+// forward's bits.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict__ x,
+                                                     const uint16_t* __restrict__ gamma, float eps,
+                                                     int64_t T, int H, float* __restrict__ dh) {
+  const int lane = threadIdx.x & 63;
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  const uint16_t* xr = x + t * H;
+  float* gr = dh + t * H;
+  const double ss = row_sumsq(xr, H, lane);
+  const double r = 1.0 / sqrt(ss / double(H) + double(eps));
+  double sg = 0.0;
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double xl = double(__uint_as_float(v[q] << 16));
+      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
+      const double gl = double(__uint_as_float(g[q] << 16));
+      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
+      sg = fma(gl * double(gr[c + 2 * q]), xl, sg);
+      sg = fma(gh * double(gr[c + 2 * q + 1]), xh, sg);
+    }
+  }
+  sg = wave_sum(sg);
+  const double c3 = r * r * r * sg / double(H);
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const double xl = double(__uint_as_float(v[q] << 16));
+      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
+      const double gl = double(__uint_as_float(g[q] << 16));
+      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
+      gr[c + 2 * q] = float(r * gl * double(gr[c + 2 * q]) - xl * c3);
+      gr[c + 2 * q + 1] = float(r * gh * double(gr[c + 2 * q + 1]) - xh * c3);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// LM head forward with fused online log-sum-exp and target gather.
+//
+// Operand A = W (vocabulary rows), operand B = hhat (token rows), so each lane
+// holds one token column and 16 vocabulary rows per 32x32 block: the
+// vocabulary reduction of a token is in-lane (64 values, fixed order), then
+// one exchange with lane l^32, then one exchange between the two waves that
+// share the token columns.  Every token goes through the same sequence of
+// operations whatever its column, so the per-tile partial (max m, sum s of
+// exp(z - m)) of a token depends only on that token's row.  Partials are
+// written per vocabulary tile and merged in tile order by k_lse_combine.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float rescale(float m, float M) {
+  return m == M ? 1.0f : __builtin_amdgcn_exp2f((m - M) * kLog2e);
+}
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
+                  const int32_t* __restrict__ target, int64_t T, int H, int V,
+                  int64_t n_vt, int64_t n_tt, float* __restrict__ pm,
+                  float* __restrict__ ps, float* __restrict__ ztgt) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  int64_t tt, vt;
+  if (!tile_of(n_tt, n_vt, tt, vt)) return;
+  const int64_t v0 = vt * kTile;
+  const int64_t t0 = tt * kTile;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile_256(W, v0, V, hhat, t0, T, H, H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int half = lane >> 5;
+  const int64_t vbase = v0 + wm * 128;
+
+  // Target gather: exactly one lane of one workgroup holds z[t, target[t]].
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + acc_col(wn, j, lane);
+    if (t < T) {
+      const int64_t tg = target[t];
+      const int64_t loc = tg - vbase;
+      if (tg >= 0 && tg < V && loc >= 0 && loc < 128) {
+        const int q = int(loc & 31);
+        if (((q >> 2) & 1) == half) {
+          const int ib = int(loc >> 5);
+          const int rb = ((q >> 3) << 2) | (q & 3);
+          float val = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (i == ib && r == rb) val = acc[i][j][r];
+          ztgt[t] = val;
+        }
+      }
+    }
+  }
+
+  // Rows past V (last vocabulary tile only) do not exist.
+  if (v0 + kTile > V) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int64_t v = v0 + acc_row(wm, i, r, lane);
+        if (v >= V) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[i][j][r] = -INFINITY;
+        }
+      }
+  }
+
+  float Mj[4], Sj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float m = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+    float s = 0.0f;
+    if (m != -INFINITY) {
+      const float mb = m * kLog2e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -mb));
+    }
+    const float mo = __shfl_xor(m, 32, 64);
+    const float so = __shfl_xor(s, 32, 64);
+    const float M = fmaxf(m, mo);
+    Mj[j] = M;
+    Sj[j] = s * rescale(m, M) + so * rescale(mo, M);
+  }
+
+  float* red = reinterpret_cast<float*>(lds);
+  if (wm == 1 && half == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      red[(wn * 4 + j) * 32 + (lane & 31)] = Mj[j];
+      red[256 + (wn * 4 + j) * 32 + (lane & 31)] = Sj[j];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && half == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t t = t0 + acc_col(wn, j, lane);
+      if (t < T) {
+        const float m1 = red[(wn * 4 + j) * 32 + (lane & 31)];
+        const float s1 = red[256 + (wn * 4 + j) * 32 + (lane & 31)];
+        const float M = fmaxf(Mj[j], m1);
+        const float S = Sj[j] * rescale(Mj[j], M) + s1 * rescale(m1, M);
+        pm[vt * T + t] = M;
+        ps[vt * T + t] = S;
+      }
+    }
+  }
+}
+
+// Merge the per-tile partials of each token in vocabulary-tile order, in
+// float64: lse = m + log sum_j s_j exp(m_j - m), logprob = z_target - lse.
+__global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ pm,
+                                                     const float* __restrict__ ps,
+                                                     const float* __restrict__ ztgt, int64_t T,
+                                                     int64_t n_vt, float* __restrict__ logprob,
+                                                     float* __restrict__ lse) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  float m = -INFINITY;
+  for (int64_t j = 0; j < n_vt; ++j) m = fmaxf(m, pm[j * T + t]);
+  double s = 0.0;
+  for (int64_t j = 0; j < n_vt; ++j) {
+    const float mj = pm[j * T + t];
+    if (mj != -INFINITY) s += double(ps[j * T + t]) * exp(double(mj) - double(m));
+  }
+  const double l = double(m) + log(s);
+  logprob[t] = float(double(ztgt[t]) - l);
+  if (lse) lse[t] = float(l);
+}
+
+__global__ void k_fill_f32(float* p, int64_t n, float v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Backward pieces.
+// ---------------------------------------------------------------------------
+
+// Wt[h][v] = W[v][h] for v < V, 0 for V <= v < Vp.  64 x 64 tiles through LDS.
+__global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict__ W, int H, int V,
+                                                     int64_t Vp, uint16_t* __restrict__ Wt) {
+  __shared__ uint16_t tile[64][65];
+  const int64_t v0 = int64_t(blockIdx.x) * 64;
+  const int h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63;
+  const int ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t v = v0 + r;
+    tile[r][tx] = (v < V) ? W[v * H + h0 + tx] : uint16_t(0);
+  }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t v = v0 + tx;
+    if (v < Vp) Wt[int64_t(h0 + r) * Vp + v] = tile[tx][r];
+  }
+}
+
+// P[t][v] = bf16(exp(z_tv - lse_t)) for a chunk of tokens, z recomputed on
+// MFMA.  Operand A = hhat (token rows), operand B = W (vocabulary rows).
+// Columns V <= v < Vp are written as 0 so the following contraction over the
+// padded vocabulary adds nothing.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_softmax_p(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
+                 const float* __restrict__ lse, int64_t TC, int H, int V, int64_t Vp,
+                 int64_t n_tt, int64_t n_vt, uint16_t* __restrict__ P) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  int64_t tt, vt;
+  if (!tile_of(n_tt, n_vt, tt, vt)) return;
+  const int64_t t0 = tt * kTile;
+  const int64_t v0 = vt * kTile;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile_256(hhat, t0, TC, W, v0, V, H, H, lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + acc_row(wm, i, r, lane);
+      const int64_t tl = t < TC ? t : TC - 1;
+      const float lb = lse[tl] * kLog2e;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t v = v0 + acc_col(wn, j, lane);
+        if (v < Vp) {
+          const float p = (v < V) ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -lb)) : 0.0f;
+          P[t * Vp + v] = f32_to_bf16_rne(p);
+        }
+      }
+    }
+  }
+}
+
+// dhhat[t][h] = coef_t * (W[target_t][h] - sum_v P[t][v] W[v][h]) for a chunk.
+// Operand A = P (token rows, K = padded vocabulary), operand B = Wt (hidden
+// rows).  The one-hot term is gathered from W exactly in fp32.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
+               const uint16_t* __restrict__ W, const int32_t* __restrict__ target,
+               const float* __restrict__ coef, int64_t TC, int H, int V, int64_t Vp,
+               int64_t n_tt, int64_t n_ht, float* __restrict__ dh) {
+  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  int64_t tt, ht;
+  if (!tile_of(n_tt, n_ht, tt, ht)) return;
+  const int64_t t0 = tt * kTile;
+  const int64_t h0 = ht * kTile;
+  f32x16 acc[4][4];
+  zero_acc(acc);
+  gemm_tile_256(P, t0, TC, Wt, h0, H, Vp, int(Vp), lds, acc);
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t t = t0 + acc_row(wm, i, r, lane);
+      if (t >= TC) continue;
+      const int64_t tg = target[t];
+      const float c = coef[t];
+      const bool ok = tg >= 0 && tg < V;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t h = h0 + acc_col(wn, j, lane);
+        if (h < H) {
+          const float wt = ok ? bf16_to_f32(W[tg * H + h]) : NAN;
+          dh[t * H + h] = c * (wt - acc[i][j][r]);
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// IS loss, coef, advantages (float64 accumulation, fixed order).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ double block_sum_256(double v, double* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) sh[tid] = sh[tid] + sh[tid + w];
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
+// One workgroup per response i.
+__global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logprob,
+                                                 const float* __restrict__ mu, int64_t T,
+                                                 const int64_t* __restrict__ ro, int R,
+                                                 const int64_t* __restrict__ go, int G,
+                                                 const float* __restrict__ reward,
+                                                 float* __restrict__ coef, float* __restrict__ adv,
+                                                 double* __restrict__ part) {
+  __shared__ double sh[256];
+  __shared__ double sA;
+  __shared__ int sok;
+  const int i = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int64_t a = ro[i];
+  const int64_t b = ro[i + 1];
+  if (tid == 0) {
+    // group of response i: the g with go[g] <= i < go[g+1] (binary search,
+    // bounded to G steps' worth of range, then verified).
+    int lo = 0, hi = G - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (go[mid] <= i) lo = mid; else hi = mid - 1;
+    }
+    const int64_t ga = go[lo];
+    const int64_t gb = go[lo + 1];
+    int ok = (ga <= i && i < gb && ga >= 0 && gb <= R) ? 1 : 0;
+    ok = ok && (a >= 0 && a < b && b <= T);
+    double A = NAN;
+    if (ok) {
+      double sr = 0.0;
+      for (int64_t k = ga; k < gb; ++k) sr += double(reward[k]);
+      A = double(reward[i]) - sr / double(gb - ga);
+    }
+    sA = A;
+    sok = ok;
+    if (adv) adv[i] = float(A);
+  }
+  __syncthreads();
+  if (!sok) {
+    if (tid == 0) part[i] = NAN;
+    return;
+  }
+  const double A = sA;
+  const double L = double(b - a);
+  const double cscale = -A / (double(R) * L);
+  double sw = 0.0;
+  for (int64_t t = a + tid; t < b; t += 256) {
+    const double w = exp(double(logprob[t]) - double(mu[t]));
+    sw += w;
+    if (coef) coef[t] = float(cscale * w);
+  }
+  sw = block_sum_256(sw, sh);
+  if (tid == 0) part[i] = A * (sw / L);
+}
+
+__global__ __launch_bounds__(256) void k_is_final(const double* __restrict__ part, int R,
+                                                  const int64_t* __restrict__ ro,
+                                                  const int64_t* __restrict__ go, int G,
+                                                  int64_t T, double* __restrict__ loss) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  for (int i = threadIdx.x; i < R; i += 256) s += part[i];
+  s = block_sum_256(s, sh);
+  if (threadIdx.x == 0) {
+    const bool ok = ro[0] == 0 && ro[R] == T && go[0] == 0 && go[G] == R;
+    *loss = ok ? -s / double(R) : NAN;
+  }
+}
+
+constexpr int64_t kD3Block = 16384;
+
+__global__ __launch_bounds__(256) void k_d3_part(const float* __restrict__ logprob,
+                                                 const float* __restrict__ mu, int64_t T,
+                                                 double* __restrict__ part) {
+  __shared__ double sh[256];
+  const int64_t a = int64_t(blockIdx.x) * kD3Block;
+  const int64_t b = a + kD3Block < T ? a + kD3Block : T;
+  double s = 0.0;
+  for (int64_t t = a + threadIdx.x; t < b; t += 256) {
+    const double d = double(logprob[t]) - double(mu[t]);
+    s += expm1(d) - d;
+  }
+  s = block_sum_256(s, sh);
+  if (threadIdx.x == 0) part[blockIdx.x] = s;
+}
+
+__global__ __launch_bounds__(256) void k_d3_final(const double* __restrict__ part, int64_t nb,
+                                                  int64_t T, double* __restrict__ d3) {
+  __shared__ double sh[256];
+  double s = 0.0;
+  for (int64_t i = threadIdx.x; i < nb; i += 256) s += part[i];
+  s = block_sum_256(s, sh);
+  if (threadIdx.x == 0) *d3 = s / double(T);
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+static inline uint32_t blocks_for(int64_t n, int64_t per) { return uint32_t(ceil_div(n, per)); }
+
+hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                              int H, uint16_t* hhat, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(blocks_for(T, 4)), dim3(256), 0, s, x, gamma, eps, T, H,
+                     hhat);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
+                             int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
+                             hipStream_t s) {
+  const int64_t n_vt = n_vocab_tiles(V);
+  const int64_t n_tt = ceil_div(T, kTile);
+  hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, NAN);
+  hipLaunchKernelGGL(k_lmhead_fwd, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s, hhat, W,
+                     target, T, H, V, n_vt, n_tt, pm, ps, ztgt);
+  return hipGetLastError();
+}
+
+hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt, int64_t T,
+                              int V, float* logprob, float* lse, hipStream_t s) {
+  hipLaunchKernelGGL(k_lse_combine, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, ps, ztgt, T,
+                     n_vocab_tiles(V), logprob, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s) {
+  const int64_t Vp = vocab_pad(V);
+  hipLaunchKernelGGL(k_transpose_w, dim3(blocks_for(Vp, 64), H / 64), dim3(256), 0, s, W, H, V, Vp,
+                     Wt);
+  return hipGetLastError();
+}
+
+hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
+                            int64_t TC, int H, int V, uint16_t* P, hipStream_t s) {
+  const int64_t n_vt = n_vocab_tiles(V);
+  const int64_t n_tt = ceil_div(TC, kTile);
+  hipLaunchKernelGGL(k_softmax_p, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s, hhat_chunk,
+                     W, lse_chunk, TC, H, V, vocab_pad(V), n_tt, n_vt, P);
+  return hipGetLastError();
+}
+
+hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t* W,
+                          const int32_t* target_chunk, const float* coef_chunk, int64_t TC, int H,
+                          int V, float* dh_chunk, hipStream_t s) {
+  const int64_t n_ht = ceil_div(H, kTile);
+  const int64_t n_tt = ceil_div(TC, kTile);
+  hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(kThreads), 0, s, P, Wt, W,
+                     target_chunk, coef_chunk, TC, H, V, vocab_pad(V), n_tt, n_ht, dh_chunk);
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
+                              int H, float* dh, hipStream_t s) {
+  hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(blocks_for(T, 4)), dim3(256), 0, s, x, gamma, eps, T, H,
+                     dh);
+  return hipGetLastError();
+}
+
+hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T, const int64_t* ro,
+                          int R, const int64_t* go, int G, const float* reward, double* loss,
+                          float* coef, float* adv, double* part, hipStream_t s) {
+  hipLaunchKernelGGL(k_is_resp, dim3(R), dim3(256), 0, s, logprob, mu, T, ro, R, go, G, reward,
+                     coef, adv, part);
+  hipLaunchKernelGGL(k_is_final, dim3(1), dim3(256), 0, s, part, R, ro, go, G, T, loss);
+  return hipGetLastError();
+}
+
+hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3, double* part,
+                     hipStream_t s) {
+  const int64_t nb = ceil_div(T, kD3Block);
+  hipLaunchKernelGGL(k_d3_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
+  hipLaunchKernelGGL(k_d3_final, dim3(1), dim3(256), 0, s, part, nb, T, d3);
+  return hipGetLastError();
+}
+
+}  // namespace rz

@@ -1,0 +1,166 @@
+"""The C ABI without a GPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import invariant_logprob_is_amd as rz
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rz.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(rz.LIB_PATH), reason="librz.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rz_[a-z0-9_]+)\s*\(", src)))
+
+
+def _gpu_present():
+    if os.path.exists("/dev/kfd"):
+        return True
+    try:
+        import torch
+        return torch.cuda.device_count() > 0
+    except Exception:
+        return False
+
+
+FAKE = 1 << 20  # a 256-byte aligned non-null address, never dereferenced
+
+
+def test_exports_every_declared_symbol():
+    L = rz.lib()
+    names = _declared()
+    assert set(names) == set(rz.SYMBOLS), "binding table and header disagree"
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_exports_are_visible_with_dlsym():
+    raw = ctypes.CDLL(rz.LIB_PATH)
+    for n in _declared():
+        assert ctypes.cast(getattr(raw, n), ctypes.c_void_p).value
+
+
+def test_version_and_status_strings():
+    assert rz.version() == (0 << 16) | (1 << 8)
+    L = rz.lib()
+    for code, text in [(0, b"ok"), (1, b"invalid argument"), (2, b"unsupported shape"),
+                       (3, b"no HIP device"), (4, b"HIP runtime error"), (5, b"workspace too small")]:
+        assert L.rz_status_string(code) == text
+    assert L.rz_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    assert rz.workspace_bytes(0, 128, 1024) == 0
+    assert rz.workspace_bytes(10, 0, 1024) == 0
+    small = rz.workspace_bytes(300, 128, 1024)
+    big = rz.workspace_bytes(300000, 1536, 151936)
+    assert 0 < small < big
+    assert small % 256 == 0 and big % 256 == 0
+    # the forward needs at least hhat + partials; the backward at least W^T + P chunk
+    assert big >= 1536 * 151936 * 2 + 32768 * 151936 * 2
+
+
+def _logprob(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, T=300, H=128, V=1024,
+             logprob=FAKE, lse=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_logprob(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["T"], a["H"],
+                               a["V"], a["logprob"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def _backward(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, lse=FAKE, coef=FAKE, T=300,
+             H=128, V=1024, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_backward(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["lse"],
+                                a["coef"], a["T"], a["H"], a["V"], a["dh"], a["ws"], a["wsb"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("fn", [_logprob, _backward])
+def test_head_argument_validation(fn):
+    for k in ("x", "gamma", "W", "target", "ws"):
+        assert fn(**{k: None}) == rz.RZ_EINVAL, k
+    assert fn(x=FAKE + 8) == rz.RZ_EINVAL          # bf16 rows need 16-byte alignment
+    assert fn(target=FAKE + 2) == rz.RZ_EINVAL
+    assert fn(ws=FAKE + 64) == rz.RZ_EINVAL        # workspace needs 256-byte alignment
+    assert fn(T=0) == rz.RZ_EINVAL
+    assert fn(T=-5) == rz.RZ_EINVAL
+    assert fn(H=0) == rz.RZ_EINVAL
+    assert fn(V=0) == rz.RZ_EINVAL
+    assert fn(eps=-1.0) == rz.RZ_EINVAL
+    assert fn(eps=float("nan")) == rz.RZ_EINVAL
+    assert fn(H=100) == rz.RZ_EUNSUPPORTED         # not a multiple of 64
+    assert fn(H=16384 + 64) == rz.RZ_EUNSUPPORTED
+    assert fn(V=(1 << 23) + 1) == rz.RZ_EUNSUPPORTED
+    assert fn(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
+
+
+def test_backward_needs_lse_coef_dh():
+    for k in ("lse", "coef", "dh"):
+        assert _backward(**{k: None}) == rz.RZ_EINVAL, k
+
+
+def _is_loss(**kw):
+    a = dict(lp=FAKE, mu=FAKE, T=300, ro=FAKE, R=16, go=FAKE, G=4, reward=FAKE, loss=FAKE,
+             coef=FAKE, adv=FAKE, ws=FAKE, wsb=1 << 30, stream=None)
+    a.update(kw)
+    return rz.lib().rz_is_loss(a["lp"], a["mu"], a["T"], a["ro"], a["R"], a["go"], a["G"],
+                               a["reward"], a["loss"], a["coef"], a["adv"], a["ws"], a["wsb"],
+                               a["stream"])
+
+
+def test_is_loss_argument_validation():
+    for k in ("lp", "mu", "ro", "go", "reward", "loss", "ws"):
+        assert _is_loss(**{k: None}) == rz.RZ_EINVAL, k
+    assert _is_loss(T=0) == rz.RZ_EINVAL
+    assert _is_loss(R=0) == rz.RZ_EINVAL
+    assert _is_loss(G=0) == rz.RZ_EINVAL
+    assert _is_loss(R=301) == rz.RZ_EINVAL         # more responses than tokens
+    assert _is_loss(G=17) == rz.RZ_EINVAL          # more groups than responses
+    assert _is_loss(ro=FAKE + 4) == rz.RZ_EINVAL   # int64 offsets need 8-byte alignment
+    assert _is_loss(wsb=16) == rz.RZ_EWORKSPACE
+
+
+def test_d3_argument_validation():
+    L = rz.lib()
+    assert L.rz_d3(None, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_d3(FAKE, FAKE, 0, FAKE, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_d3(FAKE, FAKE, 10, FAKE + 4, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 8, None) == rz.RZ_EWORKSPACE
+
+
+@pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
+def test_no_device_is_reported():
+    assert _logprob() == rz.RZ_ENODEV
+    assert _backward() == rz.RZ_ENODEV
+    assert _is_loss() == rz.RZ_ENODEV
+    assert rz.lib().rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_ENODEV
+
+
+def test_host_offset_validation():
+    rz.validate_offsets([0, 3, 5], [0, 2], 5)
+    with pytest.raises(ValueError):
+        rz.validate_offsets([0, 3, 3, 5], [0, 3], 5)   # zero-length response
+    with pytest.raises(ValueError):
+        rz.validate_offsets([0, 3, 5], [0, 2], 6)      # does not end at T
+    with pytest.raises(ValueError):
+        rz.validate_offsets([0, 3, 5], [0, 1], 5)      # groups do not cover R
+    with pytest.raises(ValueError):
+        rz.validate_offsets([1, 3, 5], [0, 2], 5)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    import importlib
+    mod = importlib.import_module("invariant_logprob_is_amd")
+    monkeypatch.setattr(mod, "_lib", None)
+    monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "nope.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        mod.lib()

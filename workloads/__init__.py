@@ -86,6 +86,7 @@ class Batch:
     H: int
     V: int
     x: np.ndarray              # [T, H] uint16 bf16 bits, pre-norm hidden states
+                               # ([T, 0] when generated without hidden states)
     gamma: np.ndarray          # [H] uint16 bf16 bits, RMSNorm weight
     W: np.ndarray              # [V, H] uint16 bf16 bits, LM-head weight (row-major)
     target: np.ndarray         # [T] int32
@@ -97,7 +98,7 @@ class Batch:
 
     @property
     def T(self) -> int:
-        return int(self.x.shape[0])
+        return int(self.resp_offsets[-1])
 
     @property
     def R(self) -> int:
@@ -118,7 +119,7 @@ def _assemble(name: str, master: int, lengths: np.ndarray, group_size: int, H: i
               noise_std: float, reward_kind: str, reward_p: float = 0.5,
               tail_frac: float = 0.0, tail_shift: float = 0.0,
               outlier_frac: float = 0.0, outlier_scale: float = 1.0,
-              with_W: bool = True) -> Batch:
+              with_W: bool = True, with_x: bool = True) -> Batch:
     T = int(lengths.sum())
     R = len(lengths)
     assert R % group_size == 0
@@ -130,7 +131,8 @@ def _assemble(name: str, master: int, lengths: np.ndarray, group_size: int, H: i
         idx = ro.choice(T, size=n_out, replace=False)
         row_scale = np.ones(T, dtype=np.float32)
         row_scale[idx] = np.float32(outlier_scale)
-    x = _normal_bf16(_rng(master, _C_X), T, H, 1.0, row_scale=row_scale)
+    x = (_normal_bf16(_rng(master, _C_X), T, H, 1.0, row_scale=row_scale) if with_x
+         else np.zeros((T, 0), np.uint16))
     gamma = _normal_bf16(_rng(master, _C_GAMMA), 1, H, 0.1, mean=1.0)[0]
     W = _normal_bf16(_rng(master, _C_W), V, H, 0.02) if with_W else None
     target = _rng(master, _C_TARGET).integers(0, V, size=T, dtype=np.int64).astype(np.int32)
@@ -165,24 +167,24 @@ def tiny() -> Batch:
     return _assemble("tiny", 0, lengths, 4, 128, 1024, 0.01, "bernoulli", 0.5)
 
 
-def qwen15b(with_W: bool = True) -> Batch:
+def qwen15b(with_W: bool = True, with_x: bool = True) -> Batch:
     """1.5B-shaped: H=1536, V=151936, 16 prompts x 8 responses with lengths
     uniform on {1024..8192} (about 590K tokens).  Lag noise N(0, 0.05)
     (lag 2-8); rewards Bernoulli(0.5)."""
     lengths = _rng(1, _C_LENGTHS).integers(1024, 8193, size=128)
-    return _assemble("qwen15b", 1, lengths, 8, 1536, 151936, 0.05, "bernoulli", 0.5, with_W=with_W)
+    return _assemble("qwen15b", 1, lengths, 8, 1536, 151936, 0.05, "bernoulli", 0.5, with_W=with_W, with_x=with_x)
 
 
-def qwen4b_lag64(with_W: bool = True) -> Batch:
+def qwen4b_lag64(with_W: bool = True, with_x: bool = True) -> Batch:
     """4B-shaped long context, lag 64: H=2560, V=151936, 8 prompts x 8
     responses of 16384 tokens.  Lag noise N(0, 0.2) with 1% of tokens shifted
     by +-3 (fair sign); rewards uniform on [0, 1)."""
     lengths = np.full(64, 16384, dtype=np.int64)
     return _assemble("qwen4b_lag64", 3, lengths, 8, 2560, 151936, 0.2, "uniform",
-                     tail_frac=0.01, tail_shift=3.0, with_W=with_W)
+                     tail_frac=0.01, tail_shift=3.0, with_W=with_W, with_x=with_x)
 
 
-def a3b30_head(with_W: bool = True) -> Batch:
+def a3b30_head(with_W: bool = True, with_x: bool = True) -> Batch:
     """30B-A3B-shaped head: H=2048, V=151936, groups of 16 responses with
     lognormal lengths (median 2048, sigma 1, rounded, clipped to [1, 32768]),
     whole groups added until T >= 2**20; 0.1% of rows scaled by 20 before the
@@ -194,7 +196,7 @@ def a3b30_head(with_W: bool = True) -> Batch:
         lengths.extend(int(v) for v in grp)
     return _assemble("a3b30_head", 4, np.asarray(lengths, dtype=np.int64), 16, 2048, 151936,
                      0.05, "bernoulli", 0.3, outlier_frac=0.001, outlier_scale=20.0,
-                     with_W=with_W)
+                     with_W=with_W, with_x=with_x)
 
 
 def rows_only(master: int, child: int, T: int, H: int, V: int):
