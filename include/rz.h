@@ -93,7 +93,7 @@ size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
  * int32 in [0, V) (out of range -> NaN logprob); logprob [T] fp32 out;
  * lse [T] fp32 out, may be NULL.  All pointers 16-byte aligned.
  * Errors: RZ_EINVAL (null pointer, T < 1, H < 1, V < 1, misalignment),
- * RZ_EUNSUPPORTED (H not a multiple of 64, H > 16384, V > 2^23),
+ * RZ_EUNSUPPORTED (H not a multiple of 64, H > 16384, V > 4000000),
  * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
 int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,

@@ -2,23 +2,39 @@
 //
 // One workgroup of 256 threads (4 waves) computes a 256 x 256 fp32 tile
 //   C[a][b] = sum_k A[a0 + a][k] * B[b0 + b][k]
-// where both operands are row-major with K contiguous ("TN"), which is the
-// natural layout of hidden states [T,H], the LM-head weight [V,H], a
-// probability block [T,V] and a transposed weight [H,V].  Waves form a 2 x 2
-// grid, each owning a 128 x 128 sub-tile held as 4 x 4 blocks of the 32x32
-// output of v_mfma_f32_32x32x16_bf16.
+// where both operands are row-major with K contiguous ("TN"), the natural
+// layout of hidden states [T,H], the LM-head weight [V,H], a probability
+// block [T,V] and a transposed weight [H,V].  Waves form a 2 x 2 grid, each
+// owning a 128 x 128 sub-tile held as 4 x 4 blocks of the 32x32 output of
+// v_mfma_f32_32x32x16_bf16 (accumulators live in AGPRs).
 //
-// Operand staging: K is consumed in stages of kBK = 64.  Each stage of both
-// operands (2 x 256 rows x 128 B) is loaded with 16-byte global loads into
-// registers while the previous stage is multiplied out of LDS, then written
-// to the other half of a double buffer.  LDS rows are padded to 144 B so the
-// 16-byte fragment reads of 32 consecutive rows are bank-conflict free.
+// Operand staging.  K is consumed in stages of kBK bf16 (2*kBK bytes per
+// row).  A stage of both operands (2 x 256 rows) is fetched with
+// buffer_load_dwordx4 ... lds, which writes straight into LDS without passing
+// through VGPRs; the LDS holds a ring of kStages stages and the loads of stage
+// s are issued while stage s - (kStages - 1) is multiplied, one load pair
+// after every few MFMAs.  Each load instruction moves 1 KB (64 lanes x 16 B,
+// lane-major in LDS); a row's 16-byte chunks are stored XOR-swizzled by a
+// function of the row so that the 16-byte fragment reads of consecutive rows
+// are bank-conflict free whether the LDS serves 8 or 16 lanes x 16 B per
+// clock:  f(row) = (row & 7) ^ ((row >> 3) & 1) for 128-byte rows (kBK = 64),
+// f(row) = ((row >> 1) ^ (row >> 3)) & 3 for 64-byte rows (kBK = 32).
 //
-// Reduction order: for every output element, the K sum is taken in the same
-// fixed order (stage 0, 1, ...; within a stage four MFMA steps of 16) no
-// matter which tile, sub-tile, block or lane the element lands in, and no
-// matter how many rows are valid.  Rows beyond the valid range are clamped to
-// the last valid row; their results are discarded by the caller.
+// Range.  Each operand tile is read through a buffer resource whose size
+// covers only the tile's valid rows; rows past the end read as zeros, so no
+// row index is ever clamped and no access leaves the operand.
+//
+// Pipeline per stage (kBK/16 MFMA steps of K=16, 16 MFMAs each): the
+// fragments of the next step are read from LDS while a step multiplies (two
+// fragment register sets, one read after each of the first eight MFMAs); the
+// wait for the next stage and the workgroup barrier sit between the two
+// halves of the last step, so the first fragments of the next stage load
+// while MFMAs run.
+//
+// Reduction order: for every output element the K sum is taken in the same
+// fixed order (stage 0, 1, ...; inside a stage steps of 16) no matter which
+// tile, sub-tile, block or lane the element lands in, and no matter how many
+// rows are valid.
 #pragma once
 
 #include "rz_internal.h"
@@ -28,11 +44,26 @@ namespace rz {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
-constexpr int kLdsStride = kBK + 8;                 // elements per LDS row
-constexpr int kStageElems = 2 * kTile * kLdsStride;  // A rows, then B rows
-constexpr int kLdsElems = 2 * kStageElems;          // double buffer
 constexpr int kThreads = 256;
+constexpr int kStages = 2;                          // LDS ring depth
+constexpr int kRowBytes = kBK * 2;                  // bytes of one operand row per stage
+constexpr int kChunks = kRowBytes / 16;             // 16-byte chunks per row (8 or 4)
+constexpr int kRowsPerLoad = 64 / kChunks;          // rows moved by one load instruction
+constexpr int kLoadsPerOp = kTile / kRowsPerLoad / 4;   // load instructions per wave per operand
+constexpr int kSteps = kBK / 16;                    // MFMA steps per stage
+constexpr int kOpStageBytes = kTile * kRowBytes;    // one operand, one stage
+constexpr int kStageBytes = 2 * kOpStageBytes;      // A then B
+constexpr int kLdsBytes = kStages * kStageBytes;    // the ring
+constexpr int kBufferFlags = 0x00020000;            // raw buffer, 32-bit data
+static_assert(kChunks == 8 || kChunks == 4, "kBK must be 64 or 32");
+static_assert(kLdsBytes <= 160 * 1024, "LDS ring too large");
+
+// Chunk swizzle of an LDS row (see above).
+__device__ __forceinline__ uint32_t swz(uint32_t row) {
+  return kChunks == 8 ? ((row & 7) ^ ((row >> 3) & 1)) : (((row >> 1) ^ (row >> 3)) & 3);
+}
 
 // Output coordinates of acc[i][j][r] inside the workgroup tile, for lane l of
 // wave (wm, wn):
@@ -54,82 +85,182 @@ __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 }
 
-// A rows [a0, a0+256) clamped to a_rows-1; B rows likewise; ld = row stride
-// (elements) of both operands; K a multiple of kBK.  Ends with a barrier, so
-// the caller may reuse `lds` immediately.
-__device__ __forceinline__ void gemm_tile_256(
-    const uint16_t* __restrict__ A, int64_t a0, int64_t a_rows,
-    const uint16_t* __restrict__ B, int64_t b0, int64_t b_rows,
-    int64_t ld, int K, uint16_t* lds, f32x16 (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-  const int lrow = tid >> 3;        // 0..31
-  const int lcol = (tid & 7) * 8;   // element offset inside a stage row
-
-  const uint16_t* pa = A + a0 * ld;
-  const uint16_t* pb = B + b0 * ld;
-  uint32_t offa[8], offb[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    const int64_t r = lrow + 32 * j;
-    const int64_t ra = (a0 + r < a_rows ? r : a_rows - 1 - a0);
-    const int64_t rb = (b0 + r < b_rows ? r : b_rows - 1 - b0);
-    offa[j] = uint32_t(ra * ld + lcol);
-    offb[j] = uint32_t(rb * ld + lcol);
-  }
-
-  u32x4 ra_[8], rb_[8];
-  auto gload = [&](int kt) {
-    const uint16_t* ka = pa + int64_t(kt) * kBK;
-    const uint16_t* kb = pb + int64_t(kt) * kBK;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      ra_[j] = *reinterpret_cast<const u32x4*>(ka + offa[j]);
-      rb_[j] = *reinterpret_cast<const u32x4*>(kb + offb[j]);
-    }
-  };
-  auto lstore = [&](int buf) {
-    uint16_t* s = lds + buf * kStageElems;
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      *reinterpret_cast<u32x4*>(s + (lrow + 32 * j) * kLdsStride + lcol) = ra_[j];
-      *reinterpret_cast<u32x4*>(s + (kTile + lrow + 32 * j) * kLdsStride + lcol) = rb_[j];
-    }
-  };
-
-  const int nk = K / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  const int frow = lane & 31;
-  const int fk = (lane >> 5) * 8;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) gload(kt + 1);
-    const uint16_t* s = lds + buf * kStageElems;
-#pragma unroll
-    for (int kk = 0; kk < kBK / 16; ++kk) {
-      bf16x8 af[4], bfr[4];
-      const int col = kk * 16 + fk;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(s + (wm * 128 + i * 32 + frow) * kLdsStride + col);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        bfr[j] = *reinterpret_cast<const bf16x8*>(s + (kTile + wn * 128 + j * 32 + frow) * kLdsStride + col);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    if (kt + 1 < nk) lstore(buf ^ 1);
-    __syncthreads();
-  }
+// Buffer resource over rows [row0, min(row0 + 256, rows)) of a row-major
+// operand with `ld` elements per row.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t row0,
+                                                            int64_t rows, int64_t ld) {
+  const int64_t left = rows - row0;
+  const int64_t valid = left < kTile ? left : kTile;
+  // The values are uniform; say so, or the compiler wraps every load that
+  // uses the resource in a per-lane loop.
+  const uint64_t p = reinterpret_cast<uint64_t>(base + row0 * ld);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane(int(valid * ld * 2));
+  void* up = reinterpret_cast<void*>((uint64_t(hi) << 32) | lo);
+  return __builtin_amdgcn_make_buffer_rsrc(up, 0, n, kBufferFlags);
 }
+
+struct GemmCore {
+  __amdgpu_buffer_rsrc_t ra, rb;
+  uint32_t va[kLoadsPerOp];  // per-lane byte offsets of the load instructions (A and B alike)
+  uint32_t aoff, boff;       // per-lane LDS byte offsets of fragment reads (step 0)
+  char* smem;
+  int wave;
+  int nk;                    // number of stages (K / kBK)
+  f32x16 acc[4][4];
+  bf16x8 fa[2][4], fb[2][4];
+
+  __device__ __forceinline__ void init(const uint16_t* A, int64_t a0, int64_t a_rows,
+                                       const uint16_t* B, int64_t b0, int64_t b_rows, int64_t ld,
+                                       char* lds) {
+    smem = lds;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: M0 needs it
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    ra = tile_rsrc(A, a0, a_rows, ld);
+    rb = tile_rsrc(B, b0, b_rows, ld);
+    // Load instruction q = wave*kLoadsPerOp + j moves rows [q*R, q*R + R)
+    // (R = kRowsPerLoad); lane -> row q*R + lane/kChunks and LDS slot
+    // lane%kChunks, which holds global chunk slot ^ swz(row).
+#pragma unroll
+    for (int j = 0; j < kLoadsPerOp; ++j) {
+      const uint32_t row = uint32_t((wave * kLoadsPerOp + j) * kRowsPerLoad + lane / kChunks);
+      const uint32_t chunk = uint32_t(lane % kChunks) ^ swz(row);
+      va[j] = row * uint32_t(ld) * 2u + chunk * 16u;
+    }
+    // Fragment rows are 32-aligned blocks + lane%32; swz depends on row mod 16.
+    const uint32_t r32 = uint32_t(lane & 31);
+    const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
+    aoff = uint32_t(wm * 128 + r32) * kRowBytes + slot0;
+    boff = uint32_t(kOpStageBytes) + uint32_t(wn * 128 + r32) * kRowBytes + slot0;
+    zero_acc(acc);
+  }
+
+  // Load pair j (one A and one B instruction) of stage kt.
+  __device__ __forceinline__ void load_pair(int kt, int j) {
+    const int soff = kt * kRowBytes;
+    char* s = smem + (kt % kStages) * kStageBytes;
+    const int q = wave * kLoadsPerOp + j;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j], soff, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kOpStageBytes + q * 1024), 16,
+                                             va[j], soff, 0, 0);
+  }
+
+  // Fragment read number q (0..7) into set F: A blocks first.
+  template <int F>
+  __device__ __forceinline__ void read_one(const char* s, uint32_t oa, uint32_t ob, int q) {
+    constexpr int kBlockBytes = 32 * kRowBytes;
+    if (q < 4)
+      fa[F][q] = *reinterpret_cast<const bf16x8*>(s + oa + q * kBlockBytes);
+    else
+      fb[F][q - 4] = *reinterpret_cast<const bf16x8*>(s + ob + (q - 4) * kBlockBytes);
+  }
+
+  template <int F>
+  __device__ __forceinline__ void mfma_one(int idx) {
+    const int i = idx >> 2, j = idx & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
+  }
+
+  // Workgroup barrier without a memory fence: the caller has already waited
+  // for exactly the loads that must be complete (a fence would also drain
+  // later stages still in flight).  The empty asm keeps the compiler from
+  // moving memory operations across it.
+  __device__ __forceinline__ static void barrier() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), vmcnt/expcnt untouched
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+  }
+
+  // Wait until at most `stages_after` stages of this wave's loads are in
+  // flight.  s_waitcnt encoding (gfx9): vmcnt[3:0], expcnt[6:4],
+  // lgkmcnt[11:8], vmcnt[5:4] at bits 15:14.
+  __device__ __forceinline__ static void wait_loads_except(int stages_after) {
+    const int n = stages_after * 2 * kLoadsPerOp;
+    switch (n) {
+      case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+      case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
+      case 16: __builtin_amdgcn_s_waitcnt(0x0F70 | (1 << 14)); break;
+      case 24: __builtin_amdgcn_s_waitcnt(0x0F70 | 8 | (1 << 14)); break;
+      case 32: __builtin_amdgcn_s_waitcnt(0x0F70 | (2 << 14)); break;
+      default: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    }
+  }
+
+  // One full MFMA step on set F, reading step kk of stage buffer s into set
+  // F^1 and issuing load pairs of stage lkt (if Load) at MFMAs 0, 4, 8, 12.
+  template <int F, bool Load>
+  __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
+    const uint32_t oa = aoff ^ uint32_t(kk << 5), ob = boff ^ uint32_t(kk << 5);
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one<F>(idx);
+      if (idx < 8) read_one<F ^ 1>(s, oa, ob, idx);
+      if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLoadsPerOp)
+        load_pair(lkt, first_pair + (idx >> 2));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Multiply out stage kt, whose step-0 fragments are in set 0.  If Load,
+  // the loads of stage kt + kStages - 1 are spread over the first steps; if
+  // More, stage kt+1 is waited for and published between the halves of the
+  // last step and its step-0 fragments are read during the second half.
+  template <bool Load, bool More>
+  __device__ __forceinline__ void stage(int kt) {
+    const char* s = smem + (kt % kStages) * kStageBytes;
+    const int lkt = kt + kStages - 1;
+    // steps 0 .. kSteps-2 (sets alternate 0,1,0,...), each reading the next step
+    step<0, Load>(s, 1, lkt, 0);
+    if (kSteps == 4) {
+      step<1, Load>(s, 2, lkt, 4);
+      step<0, false>(s, 3, lkt, 8);
+    }
+    // last step (set 1): eight MFMAs, publish stage kt+1, eight MFMAs with its reads
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) {
+      mfma_one<1>(idx);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (More) {
+      wait_loads_except(Load ? kStages - 2 : 0);
+      barrier();
+      const char* sn = smem + ((kt + 1) % kStages) * kStageBytes;
+#pragma unroll
+      for (int idx = 8; idx < 16; ++idx) {
+        mfma_one<1>(idx);
+        read_one<0>(sn, aoff, boff, idx - 8);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int idx = 8; idx < 16; ++idx) mfma_one<1>(idx);
+    }
+  }
+
+  // K must be a multiple of kBK.  Ends with no load in flight and, after the
+  // trailing barrier, no LDS read outstanding, so the caller may reuse the LDS.
+  __device__ __forceinline__ void run(int K) {
+    nk = K / kBK;
+    const int pre = nk < kStages - 1 ? nk : kStages - 1;
+    for (int st = 0; st < pre; ++st)
+#pragma unroll
+      for (int j = 0; j < kLoadsPerOp; ++j) load_pair(st, j);
+    wait_loads_except(pre - 1);
+    barrier();
+#pragma unroll
+    for (int q = 0; q < 8; ++q) read_one<0>(smem, aoff, boff, q);
+    int kt = 0;
+    for (; kt + kStages - 1 < nk; ++kt) stage<true, true>(kt);
+    for (; kt + 1 < nk; ++kt) stage<false, true>(kt);
+    stage<false, false>(kt);
+    barrier();
+  }
+};
 
 // XCD-aware tile raster.  Workgroups are dealt to the 8 XCDs round-robin by
 // id; we undo that so each XCD walks a contiguous range of the logical order,

@@ -15,7 +15,7 @@ constexpr int kTile = 256;          // operand rows per workgroup tile (both ope
 constexpr int kBK = 64;             // K elements per pipeline stage
 constexpr int kHAlign = 64;         // H must be a multiple of this
 constexpr int kMaxH = 16384;
-constexpr int64_t kMaxV = int64_t(1) << 23;  // keeps 256 * padded V below 2^32
+constexpr int64_t kMaxV = 4000000;  // keeps a 256-row tile of the padded V below 2^31 bytes
 constexpr int64_t kBwdChunk = 32768;  // tokens per backward chunk (bounds the P workspace)
 constexpr int kTokenGroup = 8;      // token tiles per L2 group in the tile raster
 

@@ -161,14 +161,15 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
                   const int32_t* __restrict__ target, int64_t T, int H, int V,
                   int64_t n_vt, int64_t n_tt, float* __restrict__ pm,
                   float* __restrict__ ps, float* __restrict__ ztgt) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   int64_t tt, vt;
   if (!tile_of(n_tt, n_vt, tt, vt)) return;
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_tile_256(W, v0, V, hhat, t0, T, H, H, lds, acc);
+  GemmCore g;
+  g.init(W, v0, V, hhat, t0, T, H, lds);
+  g.run(H);
+  f32x16 (&acc)[4][4] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -201,7 +202,7 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
     }
   }
 
-  // Rows past V (last vocabulary tile only) do not exist.
+  // Rows past V (last vocabulary tile only) do not exist (they were read as zeros).
   if (v0 + kTile > V) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -320,14 +321,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_softmax_p(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
                  const float* __restrict__ lse, int64_t TC, int H, int V, int64_t Vp,
                  int64_t n_tt, int64_t n_vt, uint16_t* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   int64_t tt, vt;
   if (!tile_of(n_tt, n_vt, tt, vt)) return;
   const int64_t t0 = tt * kTile;
   const int64_t v0 = vt * kTile;
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_tile_256(hhat, t0, TC, W, v0, V, H, H, lds, acc);
+  GemmCore g;
+  g.init(hhat, t0, TC, W, v0, V, H, lds);
+  g.run(H);
+  f32x16 (&acc)[4][4] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -360,14 +362,15 @@ void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
                const uint16_t* __restrict__ W, const int32_t* __restrict__ target,
                const float* __restrict__ coef, int64_t TC, int H, int V, int64_t Vp,
                int64_t n_tt, int64_t n_ht, float* __restrict__ dh) {
-  __shared__ __attribute__((aligned(16))) uint16_t lds[kLdsElems];
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
   int64_t tt, ht;
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  f32x16 acc[4][4];
-  zero_acc(acc);
-  gemm_tile_256(P, t0, TC, Wt, h0, H, Vp, int(Vp), lds, acc);
+  GemmCore g;
+  g.init(P, t0, TC, Wt, h0, H, Vp, lds);
+  g.run(int(Vp));
+  f32x16 (&acc)[4][4] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;

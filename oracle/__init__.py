@@ -36,7 +36,7 @@ import numpy as np
 
 __all__ = [
     "bf16_decode", "bf16_round", "rmsnorm", "logits", "log_softmax_gather",
-    "logprob", "advantages", "is_weights", "is_loss", "d3", "logit_grad",
+    "logprob", "advantages", "is_weights", "is_loss", "is_coef_rows", "d3", "logit_grad",
     "rmsnorm_backward", "backward", "learner_step",
 ]
 
@@ -189,6 +189,22 @@ def is_loss(logp, mu, resp_offsets, group_offsets, reward):
         total += A[i] * np.mean(w[a:b])
         coef[a:b] = -A[i] * w[a:b] / (R * L)
     return {"loss": -total / R, "coef": coef, "advantage": A, "w": w}
+
+
+def is_coef_rows(logp_rows, mu_rows, rows, resp_offsets, group_offsets, reward):
+    """coef_t = -A_i w_t / (R L_i) for a subset of tokens `rows` (global token
+    indices) of a batch, with that batch's structure: the same quantity
+    is_loss returns, for when the batch is too large for the oracle's forward
+    on every token.  The coefficient of a token needs only its own logpi and
+    mu plus the per-response metadata."""
+    ro = np.asarray(resp_offsets, np.int64)
+    R = len(ro) - 1
+    A = advantages(reward, group_offsets)
+    rows = np.asarray(rows, np.int64)
+    resp = np.searchsorted(ro, rows, side="right") - 1
+    L = (ro[resp + 1] - ro[resp]).astype(np.float64)
+    w, _ = is_weights(logp_rows, mu_rows)
+    return -A[resp] * w / (R * L)
 
 
 def d3(logp, mu) -> float:

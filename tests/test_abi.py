@@ -99,7 +99,7 @@ def test_head_argument_validation(fn):
     assert fn(eps=float("nan")) == rz.RZ_EINVAL
     assert fn(H=100) == rz.RZ_EUNSUPPORTED         # not a multiple of 64
     assert fn(H=16384 + 64) == rz.RZ_EUNSUPPORTED
-    assert fn(V=(1 << 23) + 1) == rz.RZ_EUNSUPPORTED
+    assert fn(V=4000001) == rz.RZ_EUNSUPPORTED
     assert fn(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
 
 

@@ -1,0 +1,41 @@
+"""Batch invariance at the 1.5B shapes (H=1536, V=151936): a fixed set of 512
+rows evaluated alone (single-row decode calls), inside batches of 7, 64, 1024
+and 65536 rows at random offsets among filler rows, and inside 2048-row
+prefill chunks.  The bits of logprob and lse must be identical across all of
+them: the kernel-mismatch term of the log-ratio decomposition is then exactly
+zero for these rows."""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from gpu_util import bf16, bits32, i32, say
+
+pytestmark = pytest.mark.gpu
+
+
+def test_invariance_sweep_15b(gpu):
+    import invariant_logprob_is_amd as rz
+    sw = workloads.invariance_sweep()
+    H, V = sw.H, sw.V
+    b = workloads.qwen15b(with_x=False)      # gamma and W of the 1.5B-shaped workload
+    g, W = bf16(b.gamma, gpu), bf16(b.W, gpu)
+    ws = torch.empty(rz.workspace_bytes(65536, H, V), dtype=torch.uint8, device=gpu)
+    n = sw.fixed_x.shape[0]
+    seen = {}
+    for label, plan in sw.batches.items():
+        lp_bits = np.zeros(n, np.uint32)
+        lse_bits = np.zeros(n, np.uint32)
+        for ids, pos, B in plan:
+            bx, bt = workloads.compose_batch(sw, ids, pos, B)
+            lp, lse = rz.logprob(bf16(bx, gpu), g, W, i32(bt, gpu), b.eps, workspace=ws)
+            lp_bits[ids] = bits32(lp)[pos]
+            lse_bits[ids] = bits32(lse)[pos]
+        say(f"  {label}: {len(plan)} calls")
+        seen[label] = (lp_bits, lse_bits)
+    ref_label = "batch1"
+    for label, (a, c) in seen.items():
+        np.testing.assert_array_equal(a, seen[ref_label][0], err_msg=f"logprob bits {label}")
+        np.testing.assert_array_equal(c, seen[ref_label][1], err_msg=f"lse bits {label}")
+    lp = seen[ref_label][0].view(np.float32)
+    assert np.all(np.isfinite(lp)) and np.all(lp <= 0)

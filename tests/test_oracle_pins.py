@@ -212,6 +212,17 @@ def test_is_loss_coef_is_finite_difference_gradient():
         assert fd == pytest.approx(out["coef"][t], rel=1e-6, abs=1e-12)
 
 
+def test_is_coef_rows_agrees_with_is_loss_on_every_row():
+    b = workloads.tiny()
+    rng = np.random.default_rng(3)
+    lp = -rng.uniform(0.5, 8, b.T)
+    mu = lp + rng.normal(0, 0.2, b.T)
+    full = oracle.is_loss(lp, mu, b.resp_offsets, b.group_offsets, b.reward)["coef"]
+    rows = np.array([0, 1, 7, b.T // 2, b.T - 1])
+    got = oracle.is_coef_rows(lp[rows], mu[rows], rows, b.resp_offsets, b.group_offsets, b.reward)
+    np.testing.assert_array_equal(got, full[rows])
+
+
 def test_d3_constant_delta_and_nonnegative():
     lp = np.full(10, -2.0)
     for c in (math.log(2.0), -0.7, 1e-5, 3.0):
