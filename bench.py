@@ -1,12 +1,14 @@
-"""Learner-head benchmark: one step = rz_logprob -> rz_is_loss -> rz_d3 ->
-rz_backward over one synthetic batch resident in HBM.
+"""Learner-head benchmark: one step = one rz_learner_step call (log-probs,
+IS loss, D3, gradient to the hidden states) over one synthetic batch resident
+in HBM.
 
     python bench.py [--steps K] [--warmup W] [--config qwen15b]
 
 Prints ONE JSON line.  `value` is learner tokens per second on one GPU;
-`roofline` covers the LM-head forward kernel (timed live with HIP events on
-the stream it runs on); `cpu_baseline` times the float64 oracle on a bounded
-sample of the same workload on the host cores.
+`roofline` covers the kernel with the largest share of the step, timed live
+with HIP events that the library records on the stream each kernel is
+launched on; `cpu_baseline` times the float64 oracle on a bounded sample of
+the same workload on the host cores.
 """
 from __future__ import annotations
 
@@ -89,7 +91,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="qwen15b",
                     choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
-    ap.add_argument("--cpu-tokens", type=int, default=2048)
+    ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -127,55 +129,55 @@ def main():
     # (a setup step, outside the timed region).
     rz.logprob(x, g, W, tgt, b.eps, workspace=ws, out=lp, lse_out=lse)
     mu = (lp + torch.from_numpy(b.lag_noise).to(dev)).contiguous()
+    outs = {"logprob": lp, "lse": lse, "dhidden": dh,
+            "coef": torch.empty(b.T, dtype=torch.float32, device=dev),
+            "loss": torch.empty(1, dtype=torch.float64, device=dev),
+            "d3": torch.empty(1, dtype=torch.float64, device=dev)}
     torch.cuda.synchronize()
-
     stream = torch.cuda.current_stream(dev)
 
-    def step(evs=None):
-        if evs is not None:
-            evs[0].record(stream)
-        rz.logprob(x, g, W, tgt, b.eps, workspace=ws, out=lp, lse_out=lse)
-        if evs is not None:
-            evs[1].record(stream)
-        loss, coef, _ = rz.is_loss(lp, mu, ro, go, reward, workspace=ws, want_advantage=False)
-        d3 = rz.d3(lp, mu, workspace=ws)
-        if evs is not None:
-            evs[2].record(stream)
-        rz.backward(x, g, W, tgt, lse, coef, b.eps, workspace=ws, out=dh)
-        if evs is not None:
-            evs[3].record(stream)
-        return loss, d3
+    def step():
+        rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs)
 
     for i in range(args.warmup):
         step()
+        torch.cuda.synchronize()
         log(f"warmup {i + 1}/{args.warmup}")
-    torch.cuda.synchronize()
 
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    rz.profile_enable(True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for i in range(args.steps):
-        loss, d3 = step(evs[i])
+        step()
+        ev[i + 1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    prof = rz.profile_read()
+    rz.profile_enable(False)
+    step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
     ms_step = 1000.0 * wall / args.steps
-    fwd_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    loss_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    bwd_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs]))
-    log(f"step {ms_step:.2f} ms (logprob {fwd_ms:.2f}, loss+d3 {loss_ms:.3f}, backward {bwd_ms:.2f}); "
-        f"loss={loss.item():.6e} d3={d3.item():.6e}")
+    log(f"step {ms_step:.2f} ms wall, events median {float(np.median(step_ms)):.2f} ms; "
+        f"loss={outs['loss'].item():.6e} d3={outs['d3'].item():.6e}")
+    for k, (tot, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        log(f"  {k:16s} {tot / args.steps:9.3f} ms/step  {n // args.steps:4d} launches/step")
 
     T, H, V = b.T, b.H, b.V
     tokens_per_s = T / (ms_step / 1000.0)
     alg_flops_token = 4.0 * H * V
-    fwd_flops = 2.0 * T * H * V          # algorithmic flops of one LM-head forward launch
-    achieved = fwd_flops / (fwd_ms / 1000.0)
+    gemm_flops_step = 2.0 * T * H * V      # algorithmic flops of each of the two GEMM kernels per step
+    kernels = {}
+    for k in ("k_lmhead_fwd", "k_dhidden"):
+        tot, n = prof.get(k, (float("nan"), 0))
+        achieved = gemm_flops_step * args.steps / (tot / 1000.0)
+        kernels[k] = {"ms_per_step": tot / args.steps, "launches_per_step": n // args.steps,
+                      "achieved_tflops": achieved / 1e12, "frac": achieved / PEAK_BF16_FLOPS}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     roofline = {
-        "kernel": "k_lmhead_fwd (LM head + online log-sum-exp; event interval spans the whole "
-                  "rz_logprob call)",
-        "bound": "mfma", "achieved": achieved / 1e12, "peak": PEAK_BF16_FLOPS / 1e12,
-        "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_FLOPS,
-        "traffic": measured_traffic("k_lmhead_fwd"),
+        "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved_tflops"],
+        "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
+        "traffic": measured_traffic(dom),
     }
     out = {
         "metric": "learner tokens/sec (fwd+bwd logprob+IS loss) and % bf16 MFMA peak, 1 GPU",
@@ -185,7 +187,7 @@ def main():
         "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}, {b.R} responses in {b.G} groups",
                    "T": T, "H": H, "V": V, "R": b.R, "G": b.G},
         "mfma_frac_algorithmic": tokens_per_s * alg_flops_token / PEAK_BF16_FLOPS,
-        "stage_ms": {"logprob": fwd_ms, "is_loss_d3": loss_ms, "backward": bwd_ms},
+        "kernels": kernels,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -168,6 +168,52 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
                 float* dhidden,
                 void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * rz_learner_step -- the whole learner head for one update in one call:
+ * rz_logprob, rz_is_loss, rz_d3 and the gradient to the hidden states, with
+ * the log-probabilities bit-identical to rz_logprob's.
+ *
+ * The batch is processed in chunks of at most 32768 tokens.  Per chunk: the
+ * forward stores e = exp(z - m_tile) (bf16) for every logit while it forms
+ * the log-sum-exp, coef_t = -A_i w_t / (R L_i) is formed as soon as the
+ * chunk's log-probabilities exist (it needs only the token's own w_t and the
+ * response metadata), e is rescaled in place to p = exp(z - lse) and
+ * contracted with W (dhhat = coef (W[target] - p W)), and the RMSNorm
+ * backward follows.  The logits are therefore computed once per step, not
+ * twice as in rz_logprob + rz_backward.
+ *
+ * Arguments as for rz_logprob, rz_is_loss, rz_d3 and rz_backward.  Outputs:
+ * logprob [T] fp32; lse [T] fp32 (may be NULL); loss [1] fp64; d3 [1] fp64;
+ * coef [T] fp32 (may be NULL); dhidden [T,H] fp32.
+ * Errors: the union of those of rz_logprob and rz_is_loss.
+ */
+int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
+                    const uint16_t* W, const int32_t* target,
+                    const float* rollout_logprob, int64_t T, int32_t H, int32_t V,
+                    const int64_t* resp_offsets, int32_t R,
+                    const int64_t* group_offsets, int32_t G,
+                    const float* reward,
+                    float* logprob, float* lse, double* loss, double* d3,
+                    float* coef, float* dhidden,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Per-kernel timing, for benchmarks (not for the caller's hot loop).
+ *
+ * rz_profile_enable(1) clears earlier records and starts recording: every
+ * kernel launch of the library is bracketed by two hipEvents recorded on the
+ * stream the kernel is launched on; rz_profile_enable(0) stops recording (and
+ * also clears).  rz_profile_count() waits for the recorded events, aggregates
+ * them by kernel name and returns the number of names (or -RZ_EHIP);
+ * rz_profile_get(i, ...) then returns name i (a library-owned string valid
+ * until the next rz_profile_* call), its summed duration in milliseconds and
+ * its launch count.  Recording creates host-side event objects; it takes a
+ * process-wide lock, so concurrent callers serialise while it is on.
+ */
+int rz_profile_enable(int on);
+int rz_profile_count(void);
+int rz_profile_get(int i, const char** name, double* total_ms, int64_t* launches);
+
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

@@ -9,6 +9,7 @@ stream.  There is no CPU fallback: if librz.so is missing, every call raises.
     loss, coef, adv = rz.is_loss(lp, mu, resp_offsets, group_offsets, reward)
     d3 = rz.d3(lp, mu)
     dx = rz.backward(x, gamma, W, target, lse, coef)
+    out = rz.learner_step(x, gamma, W, target, mu, resp_offsets, group_offsets, reward)
 
 bf16 tensors are torch.bfloat16; log-probabilities fp32; offsets int64.
 """
@@ -20,7 +21,7 @@ from typing import Optional
 
 __all__ = [
     "RzError", "lib", "version", "workspace_bytes", "logprob", "is_loss", "d3",
-    "backward", "LIB_PATH", "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
+    "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH", "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
 ]
 
@@ -43,6 +44,12 @@ SYMBOLS = {
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_backward": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "rz_learner_step": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _P, _I32, _P,
+                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+    "rz_profile_enable": (ctypes.c_int, [ctypes.c_int]),
+    "rz_profile_count": (ctypes.c_int, []),
+    "rz_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
+                                      ctypes.POINTER(ctypes.c_double), ctypes.POINTER(_I64)]),
 }
 
 _lib = None
@@ -246,3 +253,75 @@ def backward(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, workspace=Non
                            dh.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_backward", st)
     return dh
+
+
+def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offsets, reward,
+                 eps: float = 1e-6, *, workspace=None, out=None):
+    """The whole learner head for one update (rz_learner_step): per-token
+    log-probabilities (bit-identical to logprob()), the IS loss, D3, the
+    per-token loss gradient coef and dhidden, computing the logits once.
+
+    Returns a dict with logprob, lse, coef [T] fp32, loss, d3 [1] fp64 and
+    dhidden [T,H] fp32.  `out` may supply preallocated tensors for any of
+    these keys."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    _need(rollout_logprob, "rollout_logprob", torch.float32, dev, 1)
+    V = W.shape[0]
+    if (gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T
+            or rollout_logprob.shape[0] != T):
+        raise ValueError("shape mismatch among learner_step arguments")
+    if not (isinstance(resp_offsets, torch.Tensor) and resp_offsets.is_cuda):
+        validate_offsets(resp_offsets, group_offsets, T)
+    ro = _offsets_on(resp_offsets, dev, "resp_offsets")
+    go = _offsets_on(group_offsets, dev, "group_offsets")
+    R, G = ro.shape[0] - 1, go.shape[0] - 1
+    rw = _need(torch.as_tensor(reward, dtype=torch.float32).to(dev).contiguous(), "reward",
+               torch.float32, dev, 1)
+    if rw.shape[0] != R:
+        raise ValueError("reward must have one entry per response")
+    o = dict(out or {})
+    specs = {"logprob": ((T,), torch.float32), "lse": ((T,), torch.float32),
+             "coef": ((T,), torch.float32), "loss": ((1,), torch.float64),
+             "d3": ((1,), torch.float64), "dhidden": ((T, H), torch.float32)}
+    for k, (shape, dt) in specs.items():
+        if k not in o:
+            o[k] = torch.empty(shape, dtype=dt, device=dev)
+        _need(o[k], k, dt, dev, len(shape))
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    st = lib().rz_learner_step(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                               target.data_ptr(), rollout_logprob.data_ptr(), T, H, V,
+                               ro.data_ptr(), R, go.data_ptr(), G, rw.data_ptr(),
+                               o["logprob"].data_ptr(), o["lse"].data_ptr(), o["loss"].data_ptr(),
+                               o["d3"].data_ptr(), o["coef"].data_ptr(), o["dhidden"].data_ptr(),
+                               ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_learner_step", st)
+    return o
+
+
+def profile_enable(on: bool = True) -> None:
+    """Start (or stop) per-kernel event timing inside the library; clears
+    earlier records."""
+    _check("rz_profile_enable", lib().rz_profile_enable(1 if on else 0))
+
+
+def profile_read() -> dict:
+    """{kernel name: (total ms, launches)} for the launches recorded since
+    profile_enable(True).  Waits for the recorded events."""
+    n = lib().rz_profile_count()
+    if n < 0:
+        raise RzError("rz_profile_count", -n)
+    out = {}
+    for i in range(n):
+        name = ctypes.c_char_p()
+        ms = ctypes.c_double()
+        cnt = _I64()
+        _check("rz_profile_get", lib().rz_profile_get(i, ctypes.byref(name), ctypes.byref(ms),
+                                                      ctypes.byref(cnt)))
+        out[name.value.decode()] = (ms.value, cnt.value)
+    return out

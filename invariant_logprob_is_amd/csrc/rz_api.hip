@@ -80,8 +80,9 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
   float* ps = at<float>(workspace, L.ps);
   float* zt = at<float>(workspace, L.ztgt);
   hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
-  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, s);
-  if (e == hipSuccess) e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, s);
+  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, nullptr, s);
+  if (e == hipSuccess)
+    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, s);
   return status_of(e);
 }
 
@@ -150,6 +151,64 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
       e = launch_dhidden(P, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
   }
   if (e == hipSuccess) e = launch_rmsnorm_bwd(x, gamma, eps, T, H, dhidden, s);
+  return status_of(e);
+}
+
+int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                    const int32_t* target, const float* rollout_logprob, int64_t T, int32_t H,
+                    int32_t V, const int64_t* resp_offsets, int32_t R,
+                    const int64_t* group_offsets, int32_t G, const float* reward, float* logprob,
+                    float* lse, double* loss, double* d3, float* coef, float* dhidden,
+                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x || !gamma || !W || !target || !rollout_logprob || !resp_offsets || !group_offsets ||
+      !reward || !logprob || !loss || !d3 || !dhidden || !workspace)
+    return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) ||
+      !aligned4(rollout_logprob) || !aligned8(resp_offsets) || !aligned8(group_offsets) ||
+      !aligned4(reward) || !aligned4(logprob) || (lse && !aligned4(lse)) || !aligned8(loss) ||
+      !aligned8(d3) || (coef && !aligned4(coef)) || !aligned16(dhidden) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  if (R < 1 || G < 1 || int64_t(R) > T || G > R) return RZ_EINVAL;
+  const WsLayout L = ws_layout(T, H, V);
+  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint16_t* hh = at<uint16_t>(workspace, L.s_hhat);
+  uint16_t* Wt = at<uint16_t>(workspace, L.s_wt);
+  uint16_t* E = at<uint16_t>(workspace, L.s_e);
+  float* pm = at<float>(workspace, L.s_pm);
+  float* ps = at<float>(workspace, L.s_ps);
+  float* zt = at<float>(workspace, L.s_zt);
+  double* cs = at<double>(workspace, L.s_cs);
+  float* lse_ = lse ? lse : at<float>(workspace, L.s_lse);
+  float* coef_ = coef ? coef : at<float>(workspace, L.s_coef);
+  double* part = at<double>(workspace, L.s_part);
+
+  hipError_t e = launch_transpose_w(W, H, V, Wt, s);
+  if (e == hipSuccess)
+    e = launch_token_scale(resp_offsets, R, group_offsets, G, reward, T, cs, s);
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, s);
+    if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
+    if (e == hipSuccess)
+      e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse_ + c0, cs + c0,
+                             rollout_logprob + c0, coef_ + c0, s);
+    if (e == hipSuccess) e = launch_rescale_p(E, pm, lse_ + c0, tc, V, s);
+    if (e == hipSuccess)
+      e = launch_dhidden(E, Wt, W, target + c0, coef_ + c0, tc, H, V, dhidden + c0 * H, s);
+    if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
+  }
+  if (e == hipSuccess)
+    e = launch_is_loss(logprob, rollout_logprob, T, resp_offsets, R, group_offsets, G, reward,
+                       loss, nullptr, nullptr, part, s);
+  if (e == hipSuccess) e = launch_d3(logprob, rollout_logprob, T, d3, part, s);
   return status_of(e);
 }
 

@@ -16,7 +16,7 @@ constexpr int kBK = 64;             // K elements per pipeline stage
 constexpr int kHAlign = 64;         // H must be a multiple of this
 constexpr int kMaxH = 16384;
 constexpr int64_t kMaxV = 4000000;  // keeps a 256-row tile of the padded V below 2^31 bytes
-constexpr int64_t kBwdChunk = 32768;  // tokens per backward chunk (bounds the P workspace)
+constexpr int64_t kBwdChunk = 32768;  // tokens per backward / learner-step chunk (bounds the P workspace)
 constexpr int kTokenGroup = 8;      // token tiles per L2 group in the tile raster
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -35,6 +35,8 @@ struct WsLayout {
   size_t b_hhat, b_wt, b_p, bwd_end;
   // rz_is_loss / rz_d3
   size_t part, loss_end;
+  // rz_learner_step (chunks of at most kBwdChunk tokens)
+  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_cs, s_lse, s_coef, s_part, step_end;
   size_t total;
 };
 
@@ -43,6 +45,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   const int64_t Tp = round_up(T, kTile);
   const int64_t nvt = n_vocab_tiles(V);
   const int64_t Vp = vocab_pad(V);
+  const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
   size_t o = 0;
   L.hhat = o;  o = align256(o + size_t(Tp) * H * 2);
   L.pm = o;    o = align256(o + size_t(nvt) * T * 4);
@@ -52,17 +55,49 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   o = 0;
   L.b_hhat = o; o = align256(o + size_t(Tp) * H * 2);
   L.b_wt = o;   o = align256(o + size_t(H) * Vp * 2);
-  const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
   L.b_p = o;    o = align256(o + size_t(round_up(tc, kTile)) * Vp * 2);
   L.bwd_end = o;
   o = 0;
   L.part = o;   o = align256(o + size_t(T + 1) * 8);
   L.loss_end = o;
+  o = 0;
+  L.s_hhat = o; o = align256(o + size_t(tc) * H * 2);
+  L.s_wt = o;   o = align256(o + size_t(H) * Vp * 2);
+  L.s_e = o;    o = align256(o + size_t(tc) * Vp * 2);
+  L.s_pm = o;   o = align256(o + size_t(nvt) * tc * 4);
+  L.s_ps = o;   o = align256(o + size_t(nvt) * tc * 4);
+  L.s_zt = o;   o = align256(o + size_t(tc) * 4);
+  L.s_cs = o;   o = align256(o + size_t(T) * 8);
+  L.s_lse = o;  o = align256(o + size_t(T) * 4);
+  L.s_coef = o; o = align256(o + size_t(T) * 4);
+  L.s_part = o; o = align256(o + size_t(T + 1) * 8);
+  L.step_end = o;
   L.total = L.fwd_end;
   if (L.bwd_end > L.total) L.total = L.bwd_end;
   if (L.loss_end > L.total) L.total = L.loss_end;
+  if (L.step_end > L.total) L.total = L.step_end;
   return L;
 }
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel timing (rz_profile.hip).  While enabled, a ProfScope
+// records a hipEvent on the launch stream before and after the launches in
+// its scope; disabled, it costs one relaxed load.
+// ---------------------------------------------------------------------------
+bool profile_enabled();
+void profile_record(const char* name, hipStream_t s, bool start);
+
+struct ProfScope {
+  const char* name;
+  hipStream_t s;
+  bool on;
+  ProfScope(const char* n, hipStream_t st) : name(n), s(st), on(profile_enabled()) {
+    if (on) profile_record(name, s, true);
+  }
+  ~ProfScope() {
+    if (on) profile_record(name, s, false);
+  }
+};
 
 // ---------------------------------------------------------------------------
 // Kernel launchers (rz_kernels.hip).  All enqueue on `s` and return the
@@ -72,9 +107,14 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float ep
                               int64_t T, int H, uint16_t* hhat, hipStream_t s);
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
-                             hipStream_t s);
+                             uint16_t* E, hipStream_t s);
 hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt,
-                              int64_t T, int V, float* logprob, float* lse, hipStream_t s);
+                              int64_t T, int V, float* logprob, float* lse, const double* cs,
+                              const float* mu, float* coef, hipStream_t s);
+hipError_t launch_rescale_p(uint16_t* E, const float* pm, const float* lse, int64_t TC, int V,
+                            hipStream_t s);
+hipError_t launch_token_scale(const int64_t* ro, int R, const int64_t* go, int G,
+                              const float* reward, int64_t T, double* cs, hipStream_t s);
 hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s);
 hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
                             int64_t TC, int H, int V, uint16_t* P, hipStream_t s);

@@ -34,6 +34,15 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return uint16_t(u >> 16);
 }
 
+// Two floats -> two bf16 (round to nearest even) in one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  bf16x2_t v;
+  v[0] = static_cast<__bf16>(lo);
+  v[1] = static_cast<__bf16>(hi);
+  return __builtin_bit_cast(uint32_t, v);
+}
+
 // Sum over a 64-lane wavefront by xor butterfly.  At every level the two
 // partners add the same two values (a + b and b + a), so all lanes finish with
 // identical bits, and the tree does not depend on where the row sits in the
@@ -141,27 +150,33 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// LM head forward with fused online log-sum-exp and target gather.
+// LM head forward with a fused per-tile log-sum-exp and target gather.
 //
 // Operand A = W (vocabulary rows), operand B = hhat (token rows), so each lane
-// holds one token column and 16 vocabulary rows per 32x32 block: the
-// vocabulary reduction of a token is in-lane (64 values, fixed order), then
-// one exchange with lane l^32, then one exchange between the two waves that
-// share the token columns.  Every token goes through the same sequence of
-// operations whatever its column, so the per-tile partial (max m, sum s of
-// exp(z - m)) of a token depends only on that token's row.  Partials are
-// written per vocabulary tile and merged in tile order by k_lse_combine.
+// holds one token column and 16 vocabulary rows per 32x32 block.  For every
+// token of the tile the epilogue takes, in this order:
+//   1. the tile max M over its 256 vocabulary rows: in-lane over 64 values,
+//      then with lane l^32, then between the two waves sharing the column;
+//   2. e = exp(z - M) for each of its values and their sum: in-lane in a
+//      fixed order, then with lane l^32, then wave (wm=0) + wave (wm=1).
+// Every token goes through the same operations whatever its column or tile
+// position, so the partial (M, S) of a token depends only on that token's
+// row.  Partials are written per vocabulary tile and merged in tile order by
+// k_lse_combine.  With Store, the values e (rounded to bf16) are also written
+// to a [T][Vp] block, through an LDS transpose so that global stores are
+// 512-byte rows; the stored variant computes M and S with the same code.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float rescale(float m, float M) {
-  return m == M ? 1.0f : __builtin_amdgcn_exp2f((m - M) * kLog2e);
-}
+constexpr int kTrStride = kTile * 2 + 16;            // bytes per token row of the LDS transpose
+constexpr int kTrBytes = kTile * kTrStride;          // 135168
+constexpr int kFwdLds = (kTrBytes > kLdsBytes ? kTrBytes : kLdsBytes) + 2048;  // + exchange area
 
+template <bool Store>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
                   const int32_t* __restrict__ target, int64_t T, int H, int V,
-                  int64_t n_vt, int64_t n_tt, float* __restrict__ pm,
-                  float* __restrict__ ps, float* __restrict__ ztgt) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+                  int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
+                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
+  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
   int64_t tt, vt;
   if (!tile_of(n_tt, n_vt, tt, vt)) return;
   const int64_t v0 = vt * kTile;
@@ -176,7 +191,9 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int half = lane >> 5;
+  const int col = lane & 31;
   const int64_t vbase = v0 + wm * 128;
+  float* xch = reinterpret_cast<float*>(lds + kFwdLds - 2048);  // [2 waves-rows][4 j][32] x 2
 
   // Target gather: exactly one lane of one workgroup holds z[t, target[t]].
 #pragma unroll
@@ -216,7 +233,8 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
       }
   }
 
-  float Mj[4], Sj[4];
+  // 1. tile max
+  float Mj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float m = -INFINITY;
@@ -224,28 +242,51 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
-    float s = 0.0f;
-    if (m != -INFINITY) {
-      const float mb = m * kLog2e;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s += __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -mb));
-    }
-    const float mo = __shfl_xor(m, 32, 64);
-    const float so = __shfl_xor(s, 32, 64);
-    const float M = fmaxf(m, mo);
-    Mj[j] = M;
-    Sj[j] = s * rescale(m, M) + so * rescale(mo, M);
+    Mj[j] = fmaxf(m, __shfl_xor(m, 32, 64));
   }
+  if (half == 0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xch[(wm * 8 + wn * 4 + j) * 32 + col] = Mj[j];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int j = 0; j < 4; ++j) Mj[j] = fmaxf(Mj[j], xch[((wm ^ 1) * 8 + wn * 4 + j) * 32 + col]);
 
-  float* red = reinterpret_cast<float*>(lds);
+  // 2. e = exp(z - M) and its sum (order: i, then r); with Store, e is packed
+  // to bf16 and written to the LDS transpose right away (the GEMM ring is no
+  // longer read), one token block at a time to keep few values live.
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  float Sj[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    float s = 0.0f;
+    const bool finite = Mj[j] != -INFINITY;
+    const float mb = Mj[j] * kLog2e;
+    const int tl = acc_col(wn, j, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        float e[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          e[q] = finite ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r4 * 4 + q], kLog2e, -mb)) : 0.0f;
+          s += e[q];
+        }
+        if (Store) {
+          u32x2 w2;
+          w2[0] = pack_bf16x2(e[0], e[1]);
+          w2[1] = pack_bf16x2(e[2], e[3]);
+          const int vl = acc_row(wm, i, r4 * 4, lane);  // rows vl .. vl+3
+          *reinterpret_cast<u32x2*>(lds + tl * kTrStride + vl * 2) = w2;
+        }
+      }
+    Sj[j] = s + __shfl_xor(s, 32, 64);
+  }
+  __syncthreads();  // everyone has read the maxima
   if (wm == 1 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      red[(wn * 4 + j) * 32 + (lane & 31)] = Mj[j];
-      red[256 + (wn * 4 + j) * 32 + (lane & 31)] = Sj[j];
-    }
+    for (int j = 0; j < 4; ++j) xch[(wn * 4 + j) * 32 + col] = Sj[j];
   }
   __syncthreads();
   if (wm == 0 && half == 0) {
@@ -253,36 +294,70 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
     for (int j = 0; j < 4; ++j) {
       const int64_t t = t0 + acc_col(wn, j, lane);
       if (t < T) {
-        const float m1 = red[(wn * 4 + j) * 32 + (lane & 31)];
-        const float s1 = red[256 + (wn * 4 + j) * 32 + (lane & 31)];
-        const float M = fmaxf(Mj[j], m1);
-        const float S = Sj[j] * rescale(Mj[j], M) + s1 * rescale(m1, M);
-        pm[vt * T + t] = M;
-        ps[vt * T + t] = S;
+        pm[vt * T + t] = Mj[j];
+        ps[vt * T + t] = Sj[j] + xch[(wn * 4 + j) * 32 + col];
       }
+    }
+  }
+
+  if (Store) {
+    // e (bf16, token-major rows in LDS) out with 16-byte stores of whole rows
+    __syncthreads();
+#pragma unroll 4
+    for (int c = threadIdx.x; c < kTile * 32; c += kThreads) {
+      const int tl = c >> 5;
+      const int c16 = c & 31;
+      const int64_t t = t0 + tl;
+      const int64_t v = v0 + c16 * 8;
+      if (t < T && v < Vp)
+        *reinterpret_cast<u32x4*>(E + t * Vp + v) =
+            *reinterpret_cast<const u32x4*>(lds + tl * kTrStride + c16 * 16);
     }
   }
 }
 
 // Merge the per-tile partials of each token in vocabulary-tile order, in
 // float64: lse = m + log sum_j s_j exp(m_j - m), logprob = z_target - lse.
+// If cs is given (learner step), also coef = cs * exp(logprob - mu), the
+// same expression rz_is_loss evaluates.
 __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ pm,
                                                      const float* __restrict__ ps,
                                                      const float* __restrict__ ztgt, int64_t T,
                                                      int64_t n_vt, float* __restrict__ logprob,
-                                                     float* __restrict__ lse) {
+                                                     float* __restrict__ lse,
+                                                     const double* __restrict__ cs,
+                                                     const float* __restrict__ mu,
+                                                     float* __restrict__ coef) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= T) return;
+  // Both passes keep several loads in flight (the loop is latency bound);
+  // the summation order is j = 0, 1, 2, ... regardless.
   float m = -INFINITY;
+#pragma unroll 8
   for (int64_t j = 0; j < n_vt; ++j) m = fmaxf(m, pm[j * T + t]);
   double s = 0.0;
-  for (int64_t j = 0; j < n_vt; ++j) {
+  constexpr int kU = 8;
+  int64_t j = 0;
+  for (; j + kU <= n_vt; j += kU) {
+    float mj[kU], sj[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      mj[u] = pm[(j + u) * T + t];
+      sj[u] = ps[(j + u) * T + t];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (mj[u] != -INFINITY) s += double(sj[u]) * exp(double(mj[u]) - double(m));
+  }
+  for (; j < n_vt; ++j) {
     const float mj = pm[j * T + t];
     if (mj != -INFINITY) s += double(ps[j * T + t]) * exp(double(mj) - double(m));
   }
   const double l = double(m) + log(s);
-  logprob[t] = float(double(ztgt[t]) - l);
+  const float lp = float(double(ztgt[t]) - l);
+  logprob[t] = lp;
   if (lse) lse[t] = float(l);
+  if (cs) coef[t] = float(cs[t] * exp(double(lp) - double(mu[t])));
 }
 
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
@@ -397,6 +472,79 @@ void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
   }
 }
 
+// P[t][v] = bf16(e[t][v] * exp(m_tile(t, v) - lse_t)) in place, where e was
+// stored by the forward relative to the max m_tile of its 256-wide
+// vocabulary tile (pm).  One 16-byte chunk (8 values, one tile) per thread.
+__global__ __launch_bounds__(256) void k_rescale_p(uint16_t* __restrict__ E,
+                                                   const float* __restrict__ pm,
+                                                   const float* __restrict__ lse, int64_t TC,
+                                                   int64_t Vp) {
+  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_row = Vp / 8;
+  if (c >= TC * per_row) return;
+  const int64_t t = c / per_row;
+  const int64_t v = (c - t * per_row) * 8;
+  const int64_t tile = v / kTile;
+  const float sc = __builtin_amdgcn_exp2f((pm[tile * TC + t] - lse[t]) * kLog2e);
+  u32x4 q = *reinterpret_cast<const u32x4*>(E + t * Vp + v);
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    q[k] = pack_bf16x2(__uint_as_float(q[k] << 16) * sc, __uint_as_float(q[k] & 0xFFFF0000u) * sc);
+  }
+  *reinterpret_cast<u32x4*>(E + t * Vp + v) = q;
+}
+
+// Shared by the loss and the per-token scale: the group of response i (the g
+// with go[g] <= i < go[g+1]) and its advantage A_i = r_i - mean_group(r),
+// with validation of the structure (ok = 0 on anything malformed).
+__device__ void response_advantage(const int64_t* __restrict__ ro, int R,
+                                   const int64_t* __restrict__ go, int G,
+                                   const float* __restrict__ reward, int64_t T, int i,
+                                   double& A, int& ok) {
+  const int64_t a = ro[i];
+  const int64_t b = ro[i + 1];
+  int lo = 0, hi = G - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (go[mid] <= i) lo = mid; else hi = mid - 1;
+  }
+  const int64_t ga = go[lo];
+  const int64_t gb = go[lo + 1];
+  ok = (ga <= i && i < gb && ga >= 0 && gb <= R) ? 1 : 0;
+  ok = ok && (a >= 0 && a < b && b <= T);
+  A = NAN;
+  if (ok) {
+    double sr = 0.0;
+    for (int64_t k = ga; k < gb; ++k) sr += double(reward[k]);
+    A = double(reward[i]) - sr / double(gb - ga);
+  }
+}
+
+// cs[t] = -A_i / (R L_i) for every token t of response i (float64): the
+// factor that turns w_t into d loss / d logprob_t.  One workgroup per
+// response; malformed structure -> NaN for that response's tokens.
+__global__ __launch_bounds__(256) void k_token_scale(const int64_t* __restrict__ ro, int R,
+                                                     const int64_t* __restrict__ go, int G,
+                                                     const float* __restrict__ reward, int64_t T,
+                                                     double* __restrict__ cs) {
+  __shared__ double sA;
+  __shared__ int sok;
+  const int i = blockIdx.x;
+  if (threadIdx.x == 0) {
+    double A;
+    int ok;
+    response_advantage(ro, R, go, G, reward, T, i, A, ok);
+    sA = A;
+    sok = ok;
+  }
+  __syncthreads();
+  if (!sok) return;
+  const int64_t a = ro[i];
+  const int64_t b = ro[i + 1];
+  const double c = -sA / (double(R) * double(b - a));
+  for (int64_t t = a + threadIdx.x; t < b; t += 256) cs[t] = c;
+}
+
 // ---------------------------------------------------------------------------
 // IS loss, coef, advantages (float64 accumulation, fixed order).
 // ---------------------------------------------------------------------------
@@ -430,23 +578,9 @@ __global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logpr
   const int64_t a = ro[i];
   const int64_t b = ro[i + 1];
   if (tid == 0) {
-    // group of response i: the g with go[g] <= i < go[g+1] (binary search,
-    // bounded to G steps' worth of range, then verified).
-    int lo = 0, hi = G - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi + 1) >> 1;
-      if (go[mid] <= i) lo = mid; else hi = mid - 1;
-    }
-    const int64_t ga = go[lo];
-    const int64_t gb = go[lo + 1];
-    int ok = (ga <= i && i < gb && ga >= 0 && gb <= R) ? 1 : 0;
-    ok = ok && (a >= 0 && a < b && b <= T);
-    double A = NAN;
-    if (ok) {
-      double sr = 0.0;
-      for (int64_t k = ga; k < gb; ++k) sr += double(reward[k]);
-      A = double(reward[i]) - sr / double(gb - ga);
-    }
+    double A;
+    int ok;
+    response_advantage(ro, R, go, G, reward, T, i, A, ok);
     sA = A;
     sok = ok;
     if (adv) adv[i] = float(A);
@@ -516,6 +650,7 @@ static inline uint32_t blocks_for(int64_t n, int64_t per) { return uint32_t(ceil
 
 hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                               int H, uint16_t* hhat, hipStream_t s) {
+  ProfScope prof("k_rmsnorm_fwd", s);
   hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(blocks_for(T, 4)), dim3(256), 0, s, x, gamma, eps, T, H,
                      hhat);
   return hipGetLastError();
@@ -523,23 +658,48 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float ep
 
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
-                             hipStream_t s) {
+                             uint16_t* E, hipStream_t s) {
+  ProfScope prof("k_lmhead_fwd", s);
   const int64_t n_vt = n_vocab_tiles(V);
   const int64_t n_tt = ceil_div(T, kTile);
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, NAN);
-  hipLaunchKernelGGL(k_lmhead_fwd, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s, hhat, W,
-                     target, T, H, V, n_vt, n_tt, pm, ps, ztgt);
+  if (E)
+    hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+                       hhat, W, target, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E);
+  else
+    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+                       hhat, W, target, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E);
   return hipGetLastError();
 }
 
 hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt, int64_t T,
-                              int V, float* logprob, float* lse, hipStream_t s) {
+                              int V, float* logprob, float* lse, const double* cs,
+                              const float* mu, float* coef, hipStream_t s) {
+  ProfScope prof("k_lse_combine", s);
   hipLaunchKernelGGL(k_lse_combine, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, ps, ztgt, T,
-                     n_vocab_tiles(V), logprob, lse);
+                     n_vocab_tiles(V), logprob, lse, cs, mu, coef);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescale_p(uint16_t* E, const float* pm, const float* lse, int64_t TC, int V,
+                            hipStream_t s) {
+  ProfScope prof("k_rescale_p", s);
+  const int64_t Vp = vocab_pad(V);
+  const int64_t n = TC * (Vp / 8);
+  hipLaunchKernelGGL(k_rescale_p, dim3(uint32_t(ceil_div(n, 256))), dim3(256), 0, s, E, pm, lse,
+                     TC, Vp);
+  return hipGetLastError();
+}
+
+hipError_t launch_token_scale(const int64_t* ro, int R, const int64_t* go, int G,
+                              const float* reward, int64_t T, double* cs, hipStream_t s) {
+  ProfScope prof("k_token_scale", s);
+  hipLaunchKernelGGL(k_token_scale, dim3(R), dim3(256), 0, s, ro, R, go, G, reward, T, cs);
   return hipGetLastError();
 }
 
 hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s) {
+  ProfScope prof("k_transpose_w", s);
   const int64_t Vp = vocab_pad(V);
   hipLaunchKernelGGL(k_transpose_w, dim3(blocks_for(Vp, 64), H / 64), dim3(256), 0, s, W, H, V, Vp,
                      Wt);
@@ -548,6 +708,7 @@ hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hip
 
 hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
                             int64_t TC, int H, int V, uint16_t* P, hipStream_t s) {
+  ProfScope prof("k_softmax_p", s);
   const int64_t n_vt = n_vocab_tiles(V);
   const int64_t n_tt = ceil_div(TC, kTile);
   hipLaunchKernelGGL(k_softmax_p, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s, hhat_chunk,
@@ -558,6 +719,7 @@ hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const
 hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t* W,
                           const int32_t* target_chunk, const float* coef_chunk, int64_t TC, int H,
                           int V, float* dh_chunk, hipStream_t s) {
+  ProfScope prof("k_dhidden", s);
   const int64_t n_ht = ceil_div(H, kTile);
   const int64_t n_tt = ceil_div(TC, kTile);
   hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(kThreads), 0, s, P, Wt, W,
@@ -567,6 +729,7 @@ hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t*
 
 hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
                               int H, float* dh, hipStream_t s) {
+  ProfScope prof("k_rmsnorm_bwd", s);
   hipLaunchKernelGGL(k_rmsnorm_bwd, dim3(blocks_for(T, 4)), dim3(256), 0, s, x, gamma, eps, T, H,
                      dh);
   return hipGetLastError();
@@ -575,6 +738,7 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float ep
 hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T, const int64_t* ro,
                           int R, const int64_t* go, int G, const float* reward, double* loss,
                           float* coef, float* adv, double* part, hipStream_t s) {
+  ProfScope prof("k_is_loss", s);
   hipLaunchKernelGGL(k_is_resp, dim3(R), dim3(256), 0, s, logprob, mu, T, ro, R, go, G, reward,
                      coef, adv, part);
   hipLaunchKernelGGL(k_is_final, dim3(1), dim3(256), 0, s, part, R, ro, go, G, T, loss);
@@ -583,6 +747,7 @@ hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T, cons
 
 hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3, double* part,
                      hipStream_t s) {
+  ProfScope prof("k_d3", s);
   const int64_t nb = ceil_div(T, kD3Block);
   hipLaunchKernelGGL(k_d3_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
   hipLaunchKernelGGL(k_d3_final, dim3(1), dim3(256), 0, s, part, nb, T, d3);

@@ -137,12 +137,40 @@ def test_d3_argument_validation():
     assert L.rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 8, None) == rz.RZ_EWORKSPACE
 
 
+def _step(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, mu=FAKE, T=300, H=128, V=1024,
+             ro=FAKE, R=16, go=FAKE, G=4, reward=FAKE, lp=FAKE, lse=FAKE, loss=FAKE, d3=FAKE,
+             coef=FAKE, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_learner_step(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["mu"],
+                                    a["T"], a["H"], a["V"], a["ro"], a["R"], a["go"], a["G"],
+                                    a["reward"], a["lp"], a["lse"], a["loss"], a["d3"], a["coef"],
+                                    a["dh"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_learner_step_argument_validation():
+    for k in ("x", "gamma", "W", "target", "mu", "ro", "go", "reward", "lp", "loss", "d3", "dh", "ws"):
+        assert _step(**{k: None}) == rz.RZ_EINVAL, k
+    assert _step(x=FAKE + 8) == rz.RZ_EINVAL
+    assert _step(dh=FAKE + 4) == rz.RZ_EINVAL
+    assert _step(ro=FAKE + 4) == rz.RZ_EINVAL
+    assert _step(T=0) == rz.RZ_EINVAL
+    assert _step(R=0) == rz.RZ_EINVAL
+    assert _step(G=0) == rz.RZ_EINVAL
+    assert _step(R=301) == rz.RZ_EINVAL
+    assert _step(G=17) == rz.RZ_EINVAL
+    assert _step(eps=-1.0) == rz.RZ_EINVAL
+    assert _step(H=96) == rz.RZ_EUNSUPPORTED
+    assert _step(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
+
+
 @pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
 def test_no_device_is_reported():
     assert _logprob() == rz.RZ_ENODEV
     assert _backward() == rz.RZ_ENODEV
     assert _is_loss() == rz.RZ_ENODEV
     assert rz.lib().rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_ENODEV
+    assert _step() == rz.RZ_ENODEV
 
 
 def test_host_offset_validation():

@@ -1,5 +1,5 @@
 """Full-size runs in the launch configuration the benchmark times (the whole
-batch in one call per entry point), checked on sampled rows against the
+batch in one rz_learner_step call), checked on sampled rows against the
 oracle and on properties that hold at any size.
 
 The rollout log-probability here is a stand-in that neither implementation
@@ -37,12 +37,17 @@ def test_full_size_sampled_rows(gpu, cfg):
     x, g, W, t = bf16(b.x, gpu), bf16(b.gamma, gpu), bf16(b.W, gpu), i32(b.target, gpu)
     mu = f32(mu_np, gpu)
     ws = torch.empty(rz.workspace_bytes(T, H, V), dtype=torch.uint8, device=gpu)
-    lp, lse = rz.logprob(x, g, W, t, b.eps, workspace=ws)
-    loss, coef, adv = rz.is_loss(lp, mu, b.resp_offsets, b.group_offsets, b.reward, workspace=ws)
-    d3 = rz.d3(lp, mu, workspace=ws)
-    dh = rz.backward(x, g, W, t, lse, coef, b.eps, workspace=ws)
+    # the launch configuration the benchmark times: one fused step over the batch
+    out = rz.learner_step(x, g, W, t, mu, b.resp_offsets, b.group_offsets, b.reward, b.eps,
+                          workspace=ws)
+    lp, lse, coef, loss, d3, dh = (out[k] for k in ("logprob", "lse", "coef", "loss", "d3", "dhidden"))
     torch.cuda.synchronize()
     say("  gpu done")
+    # the decode-style entry point gives the same bits for every row
+    lp2, lse2 = rz.logprob(x, g, W, t, b.eps, workspace=ws)
+    assert torch.equal(lp.view(torch.int32), lp2.view(torch.int32))
+    assert torch.equal(lse.view(torch.int32), lse2.view(torch.int32))
+    _, _, adv = rz.is_loss(lp, mu, b.resp_offsets, b.group_offsets, b.reward, workspace=ws)
 
     # properties over every row
     lph = host(lp)
