@@ -84,6 +84,54 @@ def cpu_baseline(b, n_tokens: int):
                       f"D3 and backward to the hidden states in float64 numpy ({dt:.1f} s)"}
 
 
+CALIBRATION_BYTES = 1 << 28   # plain device-to-device copy run once per benchmark
+
+
+def summarize_counters(fetch_csv: str, write_csv: str):
+    """Per-launch HBM traffic of the head's kernels from rocprofv3 counter
+    collection (FETCH_SIZE and WRITE_SIZE are in KiB per dispatch), scaled by
+    what the same counters read for the calibration copy of known size."""
+    import csv
+    import collections
+
+    def per_kernel(path, counter):
+        acc = collections.defaultdict(list)
+        for r in csv.DictReader(open(path)):
+            if r["Counter_Name"] != counter:
+                continue
+            name = r["Kernel_Name"].split("(")[0].replace("void ", "").replace("rz::", "").strip()
+            acc[(name, r["Dispatch_Id"])].append(float(r["Counter_Value"]))
+        out = collections.defaultdict(list)
+        for (name, _), v in acc.items():
+            out[name].append(sum(v) * 1024.0)
+        return out
+
+    fetch = per_kernel(fetch_csv, "FETCH_SIZE")
+    write = per_kernel(write_csv, "WRITE_SIZE")
+    copy = "__amd_rocclr_copyBuffer"
+    cf = max(fetch.get(copy, [0.0])) / CALIBRATION_BYTES
+    cw = max(write.get(copy, [0.0])) / CALIBRATION_BYTES
+    os.makedirs(PROFILES, exist_ok=True)
+    sha = source_sha()
+    # the learner step launches the storing forward variant
+    for k, disp in (("k_lmhead_fwd", "k_lmhead_fwd<true>"), ("k_dhidden", "k_dhidden"),
+                    ("k_rescale_p", "k_rescale_p")):
+        if disp not in fetch or disp not in write:
+            continue
+        f = float(np.mean(fetch[disp])) / (cf or 1.0)
+        w = float(np.mean(write[disp])) / (cw or 1.0)
+        d = {"kernel": k, "source_sha": sha, "bytes_per_launch": f + w,
+             "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
+             "launches": len(fetch[disp]), "calibration": {
+                 "copy_bytes": CALIBRATION_BYTES, "fetch_factor": cf, "write_factor": cw},
+             "source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of bench.py, KiB per dispatch, "
+                       "divided by the factor the same counter reads for a copy of copy_bytes"}
+        with open(os.path.join(PROFILES, f"traffic_{k}.json"), "w") as fh:
+            json.dump(d, fh, indent=1)
+        print(f"{k}: {f / 1e9:.3f} GB fetched + {w / 1e9:.3f} GB written per launch "
+              f"(factors {cf:.3f}, {cw:.3f})")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -93,7 +141,13 @@ def main():
                     choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=4096)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
+                         "into profiles/traffic_<kernel>.json and exit")
     args = ap.parse_args()
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
                           "n_gpus": args.gpus}))
@@ -135,6 +189,11 @@ def main():
             "d3": torch.empty(1, dtype=torch.float64, device=dev)}
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
+    # a plain copy of known size: the reference for the HBM byte counters
+    cal = torch.empty(CALIBRATION_BYTES, dtype=torch.uint8, device=dev)
+    torch.empty_like(cal).copy_(cal)
+    del cal
+    torch.cuda.synchronize()
 
     def step():
         rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs)
