@@ -114,8 +114,7 @@ def summarize_counters(fetch_csv: str, write_csv: str):
     os.makedirs(PROFILES, exist_ok=True)
     sha = source_sha()
     # the learner step launches the storing forward variant
-    for k, disp in (("k_lmhead_fwd", "k_lmhead_fwd<true>"), ("k_dhidden", "k_dhidden"),
-                    ("k_rescale_p", "k_rescale_p")):
+    for k, disp in (("k_lmhead_fwd", "k_lmhead_fwd<true>"), ("k_dhidden", "k_dhidden")):
         if disp not in fetch or disp not in write:
             continue
         f = float(np.mean(fetch[disp])) / (cf or 1.0)

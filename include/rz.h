@@ -151,14 +151,18 @@ int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
  * With p_tv = exp(z_tv - lse_t), the logit gradient is coef_t (onehot - p)
  * and
  *   dhhat_t = coef_t * (W[target_t] - sum_v p_tv W_v)
- * (the one-hot term is gathered exactly in fp32; P is rounded to bf16 and
- * contracted on bf16 MFMA with fp32 accumulation in a fixed vocabulary
- * order), followed by the RMSNorm backward in fp64/fp32, the bf16 rounding
- * of hhat being treated as the identity:
+ * (the one-hot term is gathered exactly in fp32; the logits are recomputed
+ * and stored as e = 2^(z log2 e - m_j) in bf16 with m_j an integer reference
+ * per 256-wide vocabulary tile, then contracted with W on bf16 MFMA with fp32
+ * accumulation in a fixed vocabulary order, p = e 2^(m_j - m) exp(m ln 2 -
+ * lse) being applied as an exact exponent shift of e inside the contraction
+ * and a per-token factor after it), followed by the RMSNorm backward in
+ * fp64/fp32, the bf16 rounding of hhat being treated as the identity:
  *   dx_j = r gamma_j g_j - x_j r^3 (1/H) sum_k gamma_k g_k x_k.
  *
  * x, gamma, eps, W, target as for rz_logprob; lse, coef [T] fp32;
- * dhidden [T,H] fp32 out.
+ * dhidden [T,H] fp32 out.  Given the lse and coef that rz_learner_step
+ * hands out, dhidden is bit-identical to that call's.
  * Errors: as rz_logprob.
  */
 int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
@@ -174,13 +178,13 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
  * the log-probabilities bit-identical to rz_logprob's.
  *
  * The batch is processed in chunks of at most 32768 tokens.  Per chunk: the
- * forward stores e = exp(z - m_tile) (bf16) for every logit while it forms
+ * forward stores e (bf16, as in rz_backward) for every logit while it forms
  * the log-sum-exp, coef_t = -A_i w_t / (R L_i) is formed as soon as the
  * chunk's log-probabilities exist (it needs only the token's own w_t and the
- * response metadata), e is rescaled in place to p = exp(z - lse) and
- * contracted with W (dhhat = coef (W[target] - p W)), and the RMSNorm
- * backward follows.  The logits are therefore computed once per step, not
- * twice as in rz_logprob + rz_backward.
+ * response metadata), e is contracted with W with the shift to
+ * p = exp(z - lse) applied inside the contraction (dhhat = coef (W[target] -
+ * p W)), and the RMSNorm backward follows.  The logits are therefore
+ * computed once per step, not twice as in rz_logprob + rz_backward.
  *
  * Arguments as for rz_logprob, rz_is_loss, rz_d3 and rz_backward.  Outputs:
  * logprob [T] fp32; lse [T] fp32 (may be NULL); loss [1] fp64; d3 [1] fp64;

@@ -82,7 +82,8 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
   hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
   if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, nullptr, s);
   if (e == hipSuccess)
-    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, s);
+    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr, s);
   return status_of(e);
 }
 
@@ -138,19 +139,29 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
   st = check_device();
   if (st != RZ_OK) return st;
 
+  // Per chunk: the forward with the e store (its (m, S, z_target) partials
+  // are recomputed and left unused), the shift table from the given lse, then
+  // the same contraction the learner step runs.
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* hhat = at<uint16_t>(workspace, L.b_hhat);
+  uint16_t* hh = at<uint16_t>(workspace, L.b_hhat);
   uint16_t* Wt = at<uint16_t>(workspace, L.b_wt);
-  uint16_t* P = at<uint16_t>(workspace, L.b_p);
-  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
-  if (e == hipSuccess) e = launch_transpose_w(W, H, V, Wt, s);
+  uint16_t* E = at<uint16_t>(workspace, L.b_e);
+  float* pm = at<float>(workspace, L.b_pm);
+  float* ps = at<float>(workspace, L.b_ps);
+  float* zt = at<float>(workspace, L.b_zt);
+  uint32_t* D = at<uint32_t>(workspace, L.b_d);
+  float* g = at<float>(workspace, L.b_g);
+  hipError_t e = launch_transpose_w(W, H, V, Wt, s);
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
-    e = launch_softmax_p(hhat + c0 * H, W, lse + c0, tc, H, V, P, s);
+    const int64_t ds = shift_stride(tc);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, s);
+    if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
+    if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
     if (e == hipSuccess)
-      e = launch_dhidden(P, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
+      e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
+    if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
-  if (e == hipSuccess) e = launch_rmsnorm_bwd(x, gamma, eps, T, H, dhidden, s);
   return status_of(e);
 }
 
@@ -185,6 +196,8 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
   float* pm = at<float>(workspace, L.s_pm);
   float* ps = at<float>(workspace, L.s_ps);
   float* zt = at<float>(workspace, L.s_zt);
+  uint32_t* D = at<uint32_t>(workspace, L.s_d);
+  float* g = at<float>(workspace, L.s_g);
   double* cs = at<double>(workspace, L.s_cs);
   float* lse_ = lse ? lse : at<float>(workspace, L.s_lse);
   float* coef_ = coef ? coef : at<float>(workspace, L.s_coef);
@@ -195,14 +208,15 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     e = launch_token_scale(resp_offsets, R, group_offsets, G, reward, T, cs, s);
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    const int64_t ds = shift_stride(tc);
     e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, s);
     if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
     if (e == hipSuccess)
       e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse_ + c0, cs + c0,
-                             rollout_logprob + c0, coef_ + c0, s);
-    if (e == hipSuccess) e = launch_rescale_p(E, pm, lse_ + c0, tc, V, s);
+                             rollout_logprob + c0, coef_ + c0, D, ds, g, s);
     if (e == hipSuccess)
-      e = launch_dhidden(E, Wt, W, target + c0, coef_ + c0, tc, H, V, dhidden + c0 * H, s);
+      e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef_ + c0, tc, H, V, dhidden + c0 * H,
+                         s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
   if (e == hipSuccess)

@@ -101,7 +101,23 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
   return __builtin_amdgcn_make_buffer_rsrc(up, 0, n, kBufferFlags);
 }
 
-struct GemmCore {
+typedef unsigned short u16x8 __attribute__((ext_vector_type(8)));
+
+// bf16 x 2^-d for the 8 values of an A fragment, exactly, by a saturating
+// subtract of (d << 7) from each bf16 bit pattern (the values are >= 0;
+// results below the smallest normal come out as 0 or a value of the same
+// tiny order).  The low 16 bits of dd hold d << 7.
+__device__ __forceinline__ bf16x8 shift_down(bf16x8 f, uint32_t dd) {
+  const u16x8 d8 = static_cast<unsigned short>(dd);
+  return __builtin_bit_cast(bf16x8, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x8, f), d8));
+}
+
+// ShiftA: operand A holds values stored relative to a reference per row and
+// per 256-wide K block; before it is multiplied, fragment row a of K block q
+// is scaled by 2^-d(a, q), d read from dtab[q * dstride + a0 + a] (packed as
+// for shift_down; the table covers every row of the tile, valid or not).
+template <bool ShiftA>
+struct GemmCoreT {
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[kLoadsPerOp];  // per-lane byte offsets of the load instructions (A and B alike)
   uint32_t aoff, boff;       // per-lane LDS byte offsets of fragment reads (step 0)
@@ -110,6 +126,21 @@ struct GemmCore {
   int nk;                    // number of stages (K / kBK)
   f32x16 acc[4][4];
   bf16x8 fa[2][4], fb[2][4];
+  // ShiftA only: per-lane table pointer (row of block 0), current and next
+  // K block's shifts of the lane's four fragment rows.
+  const uint32_t* dsrc;
+  int64_t dstride;
+  int nq;
+  uint32_t dsh[4], dnxt[4];
+
+  __device__ __forceinline__ void set_shift(const uint32_t* dtab, int64_t stride, int64_t a0,
+                                            int64_t n_kblocks) {
+    const int lane = threadIdx.x & 63;
+    const int wm = (threadIdx.x >> 6) & 1;
+    dsrc = dtab + a0 + wm * 128 + (lane & 31);
+    dstride = stride;
+    nq = int(n_kblocks);
+  }
 
   __device__ __forceinline__ void init(const uint16_t* A, int64_t a0, int64_t a_rows,
                                        const uint16_t* B, int64_t b0, int64_t b_rows, int64_t ld,
@@ -165,6 +196,21 @@ struct GemmCore {
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
   }
 
+  // K block of 256 (4 stages of kBK = 64) whose shifts stage kt uses.
+  static constexpr int kStagesPerQ = kTile / kBK;
+
+  __device__ __forceinline__ void load_shift(int q, uint32_t (&d)[4]) {
+    const int qq = q < nq ? q : nq - 1;
+    const uint32_t* p = dsrc + qq * dstride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) d[i] = p[i * 32];
+  }
+
+  template <int F>
+  __device__ __forceinline__ void shift_frag(int i) {
+    if (ShiftA) fa[F][i] = shift_down(fa[F][i], dsh[i]);
+  }
+
   // Workgroup barrier without a memory fence: the caller has already waited
   // for exactly the loads that must be complete (a fence would also drain
   // later stages still in flight).  The empty asm keeps the compiler from
@@ -202,8 +248,11 @@ struct GemmCore {
       if (idx < 8) read_one<F ^ 1>(s, oa, ob, idx);
       if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLoadsPerOp)
         load_pair(lkt, first_pair + (idx >> 2));
+      if ((idx & 3) == 3 && idx < 15) shift_frag<F>((idx >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
+    shift_frag<F ^ 1>(0);
+    __builtin_amdgcn_sched_barrier(0);
   }
 
   // Multiply out stage kt, whose step-0 fragments are in set 0.  If Load,
@@ -214,6 +263,9 @@ struct GemmCore {
   __device__ __forceinline__ void stage(int kt) {
     const char* s = smem + (kt % kStages) * kStageBytes;
     const int lkt = kt + kStages - 1;
+    // The next K block's shifts: issued before this stage's loads, so the
+    // wait at the end of the stage covers them too.
+    if (ShiftA) load_shift(kt / kStagesPerQ + 1, dnxt);
     // steps 0 .. kSteps-2 (sets alternate 0,1,0,...), each reading the next step
     step<0, Load>(s, 1, lkt, 0);
     if (kSteps == 4) {
@@ -224,6 +276,7 @@ struct GemmCore {
 #pragma unroll
     for (int idx = 0; idx < 8; ++idx) {
       mfma_one<1>(idx);
+      if ((idx & 3) == 3) shift_frag<1>((idx >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (More) {
@@ -234,11 +287,22 @@ struct GemmCore {
       for (int idx = 8; idx < 16; ++idx) {
         mfma_one<1>(idx);
         read_one<0>(sn, aoff, boff, idx - 8);
+        if (idx == 11) shift_frag<1>(3);
         __builtin_amdgcn_sched_barrier(0);
       }
+      if (ShiftA) {
+        const bool nb = ((kt + 1) % kStagesPerQ) == 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dsh[i] = nb ? dnxt[i] : dsh[i];
+      }
+      shift_frag<0>(0);
+      __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
-      for (int idx = 8; idx < 16; ++idx) mfma_one<1>(idx);
+      for (int idx = 8; idx < 16; ++idx) {
+        mfma_one<1>(idx);
+        if (idx == 11) shift_frag<1>(3);
+      }
     }
   }
 
@@ -250,10 +314,12 @@ struct GemmCore {
     for (int st = 0; st < pre; ++st)
 #pragma unroll
       for (int j = 0; j < kLoadsPerOp; ++j) load_pair(st, j);
+    if (ShiftA) load_shift(0, dsh);
     wait_loads_except(pre - 1);
     barrier();
 #pragma unroll
     for (int q = 0; q < 8; ++q) read_one<0>(smem, aoff, boff, q);
+    shift_frag<0>(0);
     int kt = 0;
     for (; kt + kStages - 1 < nk; ++kt) stage<true, true>(kt);
     for (; kt + 1 < nk; ++kt) stage<false, true>(kt);
@@ -262,20 +328,31 @@ struct GemmCore {
   }
 };
 
+using GemmCore = GemmCoreT<false>;
+
 // XCD-aware tile raster.  Workgroups are dealt to the 8 XCDs round-robin by
-// id; we undo that so each XCD walks a contiguous range of the logical order,
-// and the logical order visits `kTokenGroup` token tiles for every tile of the
-// other operand, so the workgroups resident on one XCD share both operands in
-// that XCD's L2.  The grid is padded to a multiple of 8; returns false for the
-// padding.
+// id; we undo that so each XCD walks a contiguous range of the logical order.
+// When the other operand has few tiles (the hidden dimension of the P*W^T
+// product: 6 tiles at H = 1536), the logical order runs all of them for a
+// token tile side by side (32 / n_other token tiles at a time), so each long
+// P row block is streamed through one XCD's L2 once.  Otherwise it visits
+// `kTokenGroup` token tiles for every tile of the other operand, so the
+// workgroups resident on one XCD share both operands in that XCD's L2.  The
+// grid is padded to a multiple of 8; returns false for the padding.
 __device__ __forceinline__ bool tile_of(int64_t n_token_tiles, int64_t n_other_tiles,
                                         int64_t& tt, int64_t& ot) {
   const uint64_t nb = gridDim.x;
   const uint64_t b = blockIdx.x;
   const uint64_t w = (b & 7) * (nb >> 3) + (b >> 3);
-  const uint64_t n_tiles = uint64_t(n_token_tiles) * uint64_t(n_other_tiles);
+  const uint64_t no = uint64_t(n_other_tiles);
+  const uint64_t n_tiles = uint64_t(n_token_tiles) * no;
   if (w >= n_tiles) return false;
-  const uint64_t per_group = uint64_t(kTokenGroup) * uint64_t(n_other_tiles);
+  if (no <= 32) {
+    tt = int64_t(w / no);
+    ot = int64_t(w % no);
+    return true;
+  }
+  const uint64_t per_group = uint64_t(kTokenGroup) * no;
   const uint64_t g = w / per_group;
   const uint64_t rem = w - g * per_group;
   const uint64_t left = uint64_t(n_token_tiles) - g * kTokenGroup;

@@ -25,18 +25,21 @@ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
 
 inline int64_t n_vocab_tiles(int64_t V) { return ceil_div(V, kTile); }
 inline int64_t vocab_pad(int64_t V) { return round_up(V, kBK); }
+// Row stride of the per-tile shift table of a chunk of tc tokens: whole
+// 256-row token tiles, so the contraction reads it without a bounds check.
+inline int64_t shift_stride(int64_t tc) { return round_up(tc, kTile); }
 
 // Workspace layout; every region starts on a 256-byte boundary.  Regions of
 // different entry points overlap (calls on one workspace are ordered).
 struct WsLayout {
   // rz_logprob
   size_t hhat, pm, ps, ztgt, fwd_end;
-  // rz_backward
-  size_t b_hhat, b_wt, b_p, bwd_end;
+  // rz_backward (chunks of at most kBwdChunk tokens)
+  size_t b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, bwd_end;
   // rz_is_loss / rz_d3
   size_t part, loss_end;
   // rz_learner_step (chunks of at most kBwdChunk tokens)
-  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_cs, s_lse, s_coef, s_part, step_end;
+  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_cs, s_lse, s_coef, s_part, step_end;
   size_t total;
 };
 
@@ -46,6 +49,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   const int64_t nvt = n_vocab_tiles(V);
   const int64_t Vp = vocab_pad(V);
   const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
+  const int64_t tcp = shift_stride(tc);
   size_t o = 0;
   L.hhat = o;  o = align256(o + size_t(Tp) * H * 2);
   L.pm = o;    o = align256(o + size_t(nvt) * T * 4);
@@ -53,9 +57,14 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.ztgt = o;  o = align256(o + size_t(T) * 4);
   L.fwd_end = o;
   o = 0;
-  L.b_hhat = o; o = align256(o + size_t(Tp) * H * 2);
+  L.b_hhat = o; o = align256(o + size_t(tc) * H * 2);
   L.b_wt = o;   o = align256(o + size_t(H) * Vp * 2);
-  L.b_p = o;    o = align256(o + size_t(round_up(tc, kTile)) * Vp * 2);
+  L.b_e = o;    o = align256(o + size_t(tc) * Vp * 2);
+  L.b_pm = o;   o = align256(o + size_t(nvt) * tc * 4);
+  L.b_ps = o;   o = align256(o + size_t(nvt) * tc * 4);
+  L.b_zt = o;   o = align256(o + size_t(tc) * 4);
+  L.b_d = o;    o = align256(o + size_t(nvt) * tcp * 4);
+  L.b_g = o;    o = align256(o + size_t(tc) * 4);
   L.bwd_end = o;
   o = 0;
   L.part = o;   o = align256(o + size_t(T + 1) * 8);
@@ -67,6 +76,8 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.s_pm = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.s_ps = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.s_zt = o;   o = align256(o + size_t(tc) * 4);
+  L.s_d = o;    o = align256(o + size_t(nvt) * tcp * 4);
+  L.s_g = o;    o = align256(o + size_t(tc) * 4);
   L.s_cs = o;   o = align256(o + size_t(T) * 8);
   L.s_lse = o;  o = align256(o + size_t(T) * 4);
   L.s_coef = o; o = align256(o + size_t(T) * 4);
@@ -110,17 +121,17 @@ hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int3
                              uint16_t* E, hipStream_t s);
 hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt,
                               int64_t T, int V, float* logprob, float* lse, const double* cs,
-                              const float* mu, float* coef, hipStream_t s);
-hipError_t launch_rescale_p(uint16_t* E, const float* pm, const float* lse, int64_t TC, int V,
-                            hipStream_t s);
+                              const float* mu, float* coef, uint32_t* D, int64_t ds, float* g,
+                              hipStream_t s);
+hipError_t launch_shift_prep(const float* pm, const float* lse, int64_t T, int V, uint32_t* D,
+                             int64_t ds, float* g, hipStream_t s);
 hipError_t launch_token_scale(const int64_t* ro, int R, const int64_t* go, int G,
                               const float* reward, int64_t T, double* cs, hipStream_t s);
 hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s);
-hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
-                            int64_t TC, int H, int V, uint16_t* P, hipStream_t s);
-hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t* W,
-                          const int32_t* target_chunk, const float* coef_chunk,
-                          int64_t TC, int H, int V, float* dh_chunk, hipStream_t s);
+hipError_t launch_dhidden(const uint16_t* E, const uint32_t* D, int64_t ds, const float* g,
+                          const uint16_t* Wt, const uint16_t* W, const int32_t* target_chunk,
+                          const float* coef_chunk, int64_t TC, int H, int V, float* dh_chunk,
+                          hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float eps,
                               int64_t T, int H, float* dh, hipStream_t s);
 hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T,

@@ -8,6 +8,11 @@
 namespace rz {
 
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr double kLn2 = 0.69314718055994530942;
+
+// The integer log2 reference of a vocabulary tile with max logit M: stored
+// values are e = 2^(z log2 e - m), 1/2 < max e <= 1.
+__device__ __forceinline__ float tile_ref(float M) { return ceilf(M * kLog2e); }
 
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(uint32_t(b) << 16);
@@ -156,9 +161,12 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 // holds one token column and 16 vocabulary rows per 32x32 block.  For every
 // token of the tile the epilogue takes, in this order:
 //   1. the tile max M over its 256 vocabulary rows: in-lane over 64 values,
-//      then with lane l^32, then between the two waves sharing the column;
-//   2. e = exp(z - M) for each of its values and their sum: in-lane in a
-//      fixed order, then with lane l^32, then wave (wm=0) + wave (wm=1).
+//      then with lane l^32, then between the two waves sharing the column,
+//      and the reference m = ceil(M log2 e), an integer in log2 units;
+//   2. e = 2^(z log2 e - m) (so 1/2 < max e <= 1) for each of its values and
+//      their sum: in-lane in a fixed order, then with lane l^32, then wave
+//      (wm=0) + wave (wm=1).  The tile's partial is (M, S); m is recomputed
+//      from M with the same float expression wherever it is needed.
 // Every token goes through the same operations whatever its column or tile
 // position, so the partial (M, S) of a token depends only on that token's
 // row.  Partials are written per vocabulary tile and merged in tile order by
@@ -261,7 +269,7 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   for (int j = 0; j < 4; ++j) {
     float s = 0.0f;
     const bool finite = Mj[j] != -INFINITY;
-    const float mb = Mj[j] * kLog2e;
+    const float mb = tile_ref(Mj[j]);
     const int tl = acc_col(wn, j, lane);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -316,10 +324,41 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   }
 }
 
-// Merge the per-tile partials of each token in vocabulary-tile order, in
-// float64: lse = m + log sum_j s_j exp(m_j - m), logprob = z_target - lse.
-// If cs is given (learner step), also coef = cs * exp(logprob - mu), the
-// same expression rz_is_loss evaluates.
+// Shift table and row factor that turn the stored e of a token back into its
+// probabilities: with m = max_j m_j over the tile references,
+//   p_v = e_v 2^(m_j - m) * 2^m exp(-lse) = (e_v >> d_j) * g,
+// d_j = m - m_j (a bf16 exponent shift, 255 = flush), g = exp(m ln 2 - lse).
+// D[j * ds + t] holds d_j << 7 in both 16-bit halves.  lse is the float value
+// handed out, so the step and the stand-alone backward agree bit for bit.
+__device__ __forceinline__ void shift_tables(const float* __restrict__ pm, int64_t T, int64_t n_vt,
+                                             int64_t t, float m, float lse_f,
+                                             uint32_t* __restrict__ D, int64_t ds,
+                                             float* __restrict__ g) {
+#pragma unroll 8
+  for (int64_t j = 0; j < n_vt; ++j) {
+    const float dm = m - tile_ref(pm[j * T + t]);
+    const uint32_t d = (dm >= 0.0f && dm < 255.0f) ? uint32_t(dm) : 255u;
+    D[j * ds + t] = (d << 7) | (d << 23);
+  }
+  g[t] = float(exp(double(m) * kLn2 - double(lse_f)));
+}
+
+// max_j M_j (natural units) over the tiles of token t.
+__device__ __forceinline__ float max_tile_max(const float* __restrict__ pm, int64_t T,
+                                              int64_t n_vt, int64_t t) {
+  float M = -INFINITY;
+#pragma unroll 8
+  for (int64_t j = 0; j < n_vt; ++j) M = fmaxf(M, pm[j * T + t]);
+  return M;
+}
+
+// Merge the per-tile partials (M_j, S_j) of each token in vocabulary-tile
+// order, in float64: with m_j = tile_ref(M_j) and m = max_j m_j,
+// lse = max(m ln 2 + log sum_j S_j 2^(m_j - m), max_j M_j) (the max keeps
+// lse >= every logit against the rounding of the S_j), logprob =
+// z_target - lse.  If cs is given (learner step), also
+// coef = cs * exp(logprob - mu), the same expression rz_is_loss evaluates,
+// and if D is given the shift table and row factor of the stored e.
 __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ pm,
                                                      const float* __restrict__ ps,
                                                      const float* __restrict__ ztgt, int64_t T,
@@ -327,14 +366,15 @@ __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ p
                                                      float* __restrict__ lse,
                                                      const double* __restrict__ cs,
                                                      const float* __restrict__ mu,
-                                                     float* __restrict__ coef) {
+                                                     float* __restrict__ coef,
+                                                     uint32_t* __restrict__ D, int64_t ds,
+                                                     float* __restrict__ g) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= T) return;
   // Both passes keep several loads in flight (the loop is latency bound);
   // the summation order is j = 0, 1, 2, ... regardless.
-  float m = -INFINITY;
-#pragma unroll 8
-  for (int64_t j = 0; j < n_vt; ++j) m = fmaxf(m, pm[j * T + t]);
+  const float Mx = max_tile_max(pm, T, n_vt, t);
+  const float m = tile_ref(Mx);
   double s = 0.0;
   constexpr int kU = 8;
   int64_t j = 0;
@@ -347,17 +387,30 @@ __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ p
     }
 #pragma unroll
     for (int u = 0; u < kU; ++u)
-      if (mj[u] != -INFINITY) s += double(sj[u]) * exp(double(mj[u]) - double(m));
+      if (mj[u] != -INFINITY)
+        s += ldexp(double(sj[u]), int(fmaxf(tile_ref(mj[u]) - m, -4096.0f)));
   }
   for (; j < n_vt; ++j) {
     const float mj = pm[j * T + t];
-    if (mj != -INFINITY) s += double(ps[j * T + t]) * exp(double(mj) - double(m));
+    if (mj != -INFINITY) s += ldexp(double(ps[j * T + t]), int(fmaxf(tile_ref(mj) - m, -4096.0f)));
   }
-  const double l = double(m) + log(s);
+  const double l = fmax(double(m) * kLn2 + log(s), double(Mx));
   const float lp = float(double(ztgt[t]) - l);
+  const float lf = float(l);
   logprob[t] = lp;
-  if (lse) lse[t] = float(l);
+  if (lse) lse[t] = lf;
   if (cs) coef[t] = float(cs[t] * exp(double(lp) - double(mu[t])));
+  if (D) shift_tables(pm, T, n_vt, t, m, lf, D, ds, g);
+}
+
+// The same shift table and row factor from a given lse (stand-alone backward).
+__global__ __launch_bounds__(256) void k_shift_prep(const float* __restrict__ pm, int64_t T,
+                                                    int64_t n_vt, const float* __restrict__ lse,
+                                                    uint32_t* __restrict__ D, int64_t ds,
+                                                    float* __restrict__ g) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  shift_tables(pm, T, n_vt, t, tile_ref(max_tile_max(pm, T, n_vt, t)), lse[t], D, ds, g);
 }
 
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
@@ -388,52 +441,15 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
   }
 }
 
-// P[t][v] = bf16(exp(z_tv - lse_t)) for a chunk of tokens, z recomputed on
-// MFMA.  Operand A = hhat (token rows), operand B = W (vocabulary rows).
-// Columns V <= v < Vp are written as 0 so the following contraction over the
-// padded vocabulary adds nothing.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_softmax_p(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
-                 const float* __restrict__ lse, int64_t TC, int H, int V, int64_t Vp,
-                 int64_t n_tt, int64_t n_vt, uint16_t* __restrict__ P) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
-  int64_t tt, vt;
-  if (!tile_of(n_tt, n_vt, tt, vt)) return;
-  const int64_t t0 = tt * kTile;
-  const int64_t v0 = vt * kTile;
-  GemmCore g;
-  g.init(hhat, t0, TC, W, v0, V, H, lds);
-  g.run(H);
-  f32x16 (&acc)[4][4] = g.acc;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + acc_row(wm, i, r, lane);
-      const int64_t tl = t < TC ? t : TC - 1;
-      const float lb = lse[tl] * kLog2e;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t v = v0 + acc_col(wn, j, lane);
-        if (v < Vp) {
-          const float p = (v < V) ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r], kLog2e, -lb)) : 0.0f;
-          P[t * Vp + v] = f32_to_bf16_rne(p);
-        }
-      }
-    }
-  }
-}
-
-// dhhat[t][h] = coef_t * (W[target_t][h] - sum_v P[t][v] W[v][h]) for a chunk.
-// Operand A = P (token rows, K = padded vocabulary), operand B = Wt (hidden
+// dhhat[t][h] = coef_t * (W[target_t][h] - sum_v p_tv W[v][h]) for a chunk,
+// with p_tv = (E[t][v] >> d(t, v / 256)) * g_t rebuilt from the stored e
+// (k_lmhead_fwd) and the shift table (shift_tables): the exponent shift is
+// applied to the A fragments inside the contraction, g_t to its result.
+// Operand A = E (token rows, K = padded vocabulary), operand B = Wt (hidden
 // rows).  The one-hot term is gathered from W exactly in fp32.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
+void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
+               const float* __restrict__ gf, const uint16_t* __restrict__ Wt,
                const uint16_t* __restrict__ W, const int32_t* __restrict__ target,
                const float* __restrict__ coef, int64_t TC, int H, int V, int64_t Vp,
                int64_t n_tt, int64_t n_ht, float* __restrict__ dh) {
@@ -442,8 +458,9 @@ void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  GemmCore g;
-  g.init(P, t0, TC, Wt, h0, H, Vp, lds);
+  GemmCoreT<true> g;
+  g.init(E, t0, TC, Wt, h0, H, Vp, lds);
+  g.set_shift(D, ds, t0, (int64_t(V) + kTile - 1) / kTile);
   g.run(int(Vp));
   f32x16 (&acc)[4][4] = g.acc;
 
@@ -459,39 +476,18 @@ void k_dhidden(const uint16_t* __restrict__ P, const uint16_t* __restrict__ Wt,
       if (t >= TC) continue;
       const int64_t tg = target[t];
       const float c = coef[t];
+      const float gt = gf[t];
       const bool ok = tg >= 0 && tg < V;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int64_t h = h0 + acc_col(wn, j, lane);
         if (h < H) {
           const float wt = ok ? bf16_to_f32(W[tg * H + h]) : NAN;
-          dh[t * H + h] = c * (wt - acc[i][j][r]);
+          dh[t * H + h] = c * (wt - gt * acc[i][j][r]);
         }
       }
     }
   }
-}
-
-// P[t][v] = bf16(e[t][v] * exp(m_tile(t, v) - lse_t)) in place, where e was
-// stored by the forward relative to the max m_tile of its 256-wide
-// vocabulary tile (pm).  One 16-byte chunk (8 values, one tile) per thread.
-__global__ __launch_bounds__(256) void k_rescale_p(uint16_t* __restrict__ E,
-                                                   const float* __restrict__ pm,
-                                                   const float* __restrict__ lse, int64_t TC,
-                                                   int64_t Vp) {
-  const int64_t c = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t per_row = Vp / 8;
-  if (c >= TC * per_row) return;
-  const int64_t t = c / per_row;
-  const int64_t v = (c - t * per_row) * 8;
-  const int64_t tile = v / kTile;
-  const float sc = __builtin_amdgcn_exp2f((pm[tile * TC + t] - lse[t]) * kLog2e);
-  u32x4 q = *reinterpret_cast<const u32x4*>(E + t * Vp + v);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    q[k] = pack_bf16x2(__uint_as_float(q[k] << 16) * sc, __uint_as_float(q[k] & 0xFFFF0000u) * sc);
-  }
-  *reinterpret_cast<u32x4*>(E + t * Vp + v) = q;
 }
 
 // Shared by the loss and the per-token scale: the group of response i (the g
@@ -674,20 +670,19 @@ hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int3
 
 hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt, int64_t T,
                               int V, float* logprob, float* lse, const double* cs,
-                              const float* mu, float* coef, hipStream_t s) {
+                              const float* mu, float* coef, uint32_t* D, int64_t ds, float* g,
+                              hipStream_t s) {
   ProfScope prof("k_lse_combine", s);
   hipLaunchKernelGGL(k_lse_combine, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, ps, ztgt, T,
-                     n_vocab_tiles(V), logprob, lse, cs, mu, coef);
+                     n_vocab_tiles(V), logprob, lse, cs, mu, coef, D, ds, g);
   return hipGetLastError();
 }
 
-hipError_t launch_rescale_p(uint16_t* E, const float* pm, const float* lse, int64_t TC, int V,
-                            hipStream_t s) {
-  ProfScope prof("k_rescale_p", s);
-  const int64_t Vp = vocab_pad(V);
-  const int64_t n = TC * (Vp / 8);
-  hipLaunchKernelGGL(k_rescale_p, dim3(uint32_t(ceil_div(n, 256))), dim3(256), 0, s, E, pm, lse,
-                     TC, Vp);
+hipError_t launch_shift_prep(const float* pm, const float* lse, int64_t T, int V, uint32_t* D,
+                             int64_t ds, float* g, hipStream_t s) {
+  ProfScope prof("k_shift_prep", s);
+  hipLaunchKernelGGL(k_shift_prep, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, T,
+                     n_vocab_tiles(V), lse, D, ds, g);
   return hipGetLastError();
 }
 
@@ -706,24 +701,16 @@ hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hip
   return hipGetLastError();
 }
 
-hipError_t launch_softmax_p(const uint16_t* hhat_chunk, const uint16_t* W, const float* lse_chunk,
-                            int64_t TC, int H, int V, uint16_t* P, hipStream_t s) {
-  ProfScope prof("k_softmax_p", s);
-  const int64_t n_vt = n_vocab_tiles(V);
-  const int64_t n_tt = ceil_div(TC, kTile);
-  hipLaunchKernelGGL(k_softmax_p, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s, hhat_chunk,
-                     W, lse_chunk, TC, H, V, vocab_pad(V), n_tt, n_vt, P);
-  return hipGetLastError();
-}
-
-hipError_t launch_dhidden(const uint16_t* P, const uint16_t* Wt, const uint16_t* W,
-                          const int32_t* target_chunk, const float* coef_chunk, int64_t TC, int H,
-                          int V, float* dh_chunk, hipStream_t s) {
+hipError_t launch_dhidden(const uint16_t* E, const uint32_t* D, int64_t ds, const float* g,
+                          const uint16_t* Wt, const uint16_t* W, const int32_t* target_chunk,
+                          const float* coef_chunk, int64_t TC, int H, int V, float* dh_chunk,
+                          hipStream_t s) {
   ProfScope prof("k_dhidden", s);
   const int64_t n_ht = ceil_div(H, kTile);
   const int64_t n_tt = ceil_div(TC, kTile);
-  hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(kThreads), 0, s, P, Wt, W,
-                     target_chunk, coef_chunk, TC, H, V, vocab_pad(V), n_tt, n_ht, dh_chunk);
+  hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(kThreads), 0, s, E, D, ds, g,
+                     Wt, W, target_chunk, coef_chunk, TC, H, V, vocab_pad(V), n_tt, n_ht,
+                     dh_chunk);
   return hipGetLastError();
 }
 
