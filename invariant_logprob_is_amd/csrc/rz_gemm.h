@@ -116,10 +116,24 @@ __device__ __forceinline__ bf16x8 shift_down(bf16x8 f, uint32_t dd) {
 // per 256-wide K block; before it is multiplied, fragment row a of K block q
 // is scaled by 2^-d(a, q), d read from dtab[q * dstride + a0 + a] (packed as
 // for shift_down; the table covers every row of the tile, valid or not).
-template <bool ShiftA>
+//
+// ANative: operand A is stored in fragment order instead of row-major.  For
+// each 256-row tile, K step ks (16 wide) and 32-row block mb, the 1 KB
+// fragment [ks][mb] holds lane l's eight K values k = 8 (l / 32) .. + 7 of
+// row 32 mb + l % 32 at byte 16 l; fragments follow each other in
+// ([tile][ks][mb]) order (frag_offset).  A stage of A is then one contiguous
+// 32 KB block, loaded as 1 KB pieces and read back at lane * 16 with no
+// swizzle.  Rows past the end of the operand hold whatever the producer left
+// there; they only reach the matching output rows.
+__host__ __device__ constexpr int64_t frag_offset(int64_t tile, int64_t ks, int64_t mb,
+                                                  int64_t n_ks) {
+  return ((tile * n_ks + ks) * 8 + mb) * 1024;  // bytes
+}
+
+template <bool ShiftA, bool ANative = false>
 struct GemmCoreT {
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[kLoadsPerOp];  // per-lane byte offsets of the load instructions (A and B alike)
+  uint32_t va[kLoadsPerOp];  // per-lane byte offsets of the load instructions (B, and A if row-major)
   uint32_t aoff, boff;       // per-lane LDS byte offsets of fragment reads (step 0)
   char* smem;
   int wave;
@@ -151,7 +165,19 @@ struct GemmCoreT {
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: M0 needs it
     const int wm = wave & 1;
     const int wn = wave >> 1;
-    ra = tile_rsrc(A, a0, a_rows, ld);
+    if (ANative) {
+      // the whole fragment block of this 256-row tile (a0 is a multiple of 256)
+      const int64_t n_ks = ld / 16;
+      const uint64_t p = reinterpret_cast<uint64_t>(
+          reinterpret_cast<const char*>(A) + frag_offset(a0 / kTile, 0, 0, n_ks));
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+      const int n = __builtin_amdgcn_readfirstlane(int(n_ks * 8 * 1024));
+      ra = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                             n, kBufferFlags);
+    } else {
+      ra = tile_rsrc(A, a0, a_rows, ld);
+    }
     rb = tile_rsrc(B, b0, b_rows, ld);
     // Load instruction q = wave*kLoadsPerOp + j moves rows [q*R, q*R + R)
     // (R = kRowsPerLoad); lane -> row q*R + lane/kChunks and LDS slot
@@ -165,7 +191,8 @@ struct GemmCoreT {
     // Fragment rows are 32-aligned blocks + lane%32; swz depends on row mod 16.
     const uint32_t r32 = uint32_t(lane & 31);
     const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
-    aoff = uint32_t(wm * 128 + r32) * kRowBytes + slot0;
+    aoff = ANative ? uint32_t(wm * 4 * 1024 + lane * 16)
+                   : uint32_t(wm * 128 + r32) * kRowBytes + slot0;
     boff = uint32_t(kOpStageBytes) + uint32_t(wn * 128 + r32) * kRowBytes + slot0;
     zero_acc(acc);
   }
@@ -175,7 +202,13 @@ struct GemmCoreT {
     const int soff = kt * kRowBytes;
     char* s = smem + (kt % kStages) * kStageBytes;
     const int q = wave * kLoadsPerOp + j;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j], soff, 0, 0);
+    if (ANative)  // piece q of the stage's contiguous 32 KB block, lane-major as stored
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
+                                               uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
+                                               kt * kOpStageBytes, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j], soff, 0,
+                                               0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kOpStageBytes + q * 1024), 16,
                                              va[j], soff, 0, 0);
   }
@@ -184,8 +217,9 @@ struct GemmCoreT {
   template <int F>
   __device__ __forceinline__ void read_one(const char* s, uint32_t oa, uint32_t ob, int q) {
     constexpr int kBlockBytes = 32 * kRowBytes;
+    constexpr int kABlockBytes = ANative ? 1024 : kBlockBytes;
     if (q < 4)
-      fa[F][q] = *reinterpret_cast<const bf16x8*>(s + oa + q * kBlockBytes);
+      fa[F][q] = *reinterpret_cast<const bf16x8*>(s + oa + q * kABlockBytes);
     else
       fb[F][q - 4] = *reinterpret_cast<const bf16x8*>(s + ob + (q - 4) * kBlockBytes);
   }
@@ -241,7 +275,8 @@ struct GemmCoreT {
   // F^1 and issuing load pairs of stage lkt (if Load) at MFMAs 0, 4, 8, 12.
   template <int F, bool Load>
   __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
-    const uint32_t oa = aoff ^ uint32_t(kk << 5), ob = boff ^ uint32_t(kk << 5);
+    const uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
+    const uint32_t ob = boff ^ uint32_t(kk << 5);
 #pragma unroll
     for (int idx = 0; idx < 16; ++idx) {
       mfma_one<F>(idx);

@@ -59,7 +59,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   o = 0;
   L.b_hhat = o; o = align256(o + size_t(tc) * H * 2);
   L.b_wt = o;   o = align256(o + size_t(H) * Vp * 2);
-  L.b_e = o;    o = align256(o + size_t(tc) * Vp * 2);
+  L.b_e = o;    o = align256(o + size_t(tcp) * Vp * 2);
   L.b_pm = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.b_ps = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.b_zt = o;   o = align256(o + size_t(tc) * 4);
@@ -72,7 +72,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   o = 0;
   L.s_hhat = o; o = align256(o + size_t(tc) * H * 2);
   L.s_wt = o;   o = align256(o + size_t(H) * Vp * 2);
-  L.s_e = o;    o = align256(o + size_t(tc) * Vp * 2);
+  L.s_e = o;    o = align256(o + size_t(tcp) * Vp * 2);
   L.s_pm = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.s_ps = o;   o = align256(o + size_t(nvt) * tc * 4);
   L.s_zt = o;   o = align256(o + size_t(tc) * 4);

@@ -171,12 +171,17 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 // position, so the partial (M, S) of a token depends only on that token's
 // row.  Partials are written per vocabulary tile and merged in tile order by
 // k_lse_combine.  With Store, the values e (rounded to bf16) are also written
-// to a [T][Vp] block, through an LDS transpose so that global stores are
-// 512-byte rows; the stored variant computes M and S with the same code.
+// out, straight from registers, in the fragment order of the contraction that
+// consumes them (frag_offset, token tiles x 16-wide vocabulary steps):
+// lanes l and l+32 of a 32x32 block hold vocabulary rows 8q..8q+3 and
+// 8q+4..8q+7 of token l % 32, so one v_permlane32_swap per register pair
+// (q, q+1) leaves lane l < 32 with rows 8q..8q+7 and lane l + 32 with rows
+// 8q+8..8q+15: exactly one A fragment, stored as a contiguous 1 KB per wave.
+// Rows V <= v < Vp hold 0; token columns past T hold finite values that the
+// contraction only carries into rows it does not write.  The stored variant
+// computes M and S with the same code.
 // ---------------------------------------------------------------------------
-constexpr int kTrStride = kTile * 2 + 16;            // bytes per token row of the LDS transpose
-constexpr int kTrBytes = kTile * kTrStride;          // 135168
-constexpr int kFwdLds = (kTrBytes > kLdsBytes ? kTrBytes : kLdsBytes) + 2048;  // + exchange area
+constexpr int kFwdLds = kLdsBytes + 2048;  // the GEMM ring + the exchange area
 
 template <bool Store>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -260,19 +265,20 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
 #pragma unroll
   for (int j = 0; j < 4; ++j) Mj[j] = fmaxf(Mj[j], xch[((wm ^ 1) * 8 + wn * 4 + j) * 32 + col]);
 
-  // 2. e = exp(z - M) and its sum (order: i, then r); with Store, e is packed
-  // to bf16 and written to the LDS transpose right away (the GEMM ring is no
-  // longer read), one token block at a time to keep few values live.
+  // 2. e = 2^(z log2 e - m) and its sum (order: i, then r); with Store, e is
+  // packed to bf16 and written out as A fragments (see above), one 32x32
+  // block at a time to keep few values live.
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  const int64_t n_ks = Vp / 16;
   float Sj[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float s = 0.0f;
     const bool finite = Mj[j] != -INFINITY;
     const float mb = tile_ref(Mj[j]);
-    const int tl = acc_col(wn, j, lane);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      u32x2 X[4];
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
         float e[4];
@@ -282,13 +288,29 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
           s += e[q];
         }
         if (Store) {
-          u32x2 w2;
-          w2[0] = pack_bf16x2(e[0], e[1]);
-          w2[1] = pack_bf16x2(e[2], e[3]);
-          const int vl = acc_row(wm, i, r4 * 4, lane);  // rows vl .. vl+3
-          *reinterpret_cast<u32x2*>(lds + tl * kTrStride + vl * 2) = w2;
+          X[r4][0] = pack_bf16x2(e[0], e[1]);
+          X[r4][1] = pack_bf16x2(e[2], e[3]);
         }
       }
+      if (Store) {
+        const int64_t ks0 = (v0 + wm * 128 + i * 32) / 16;
+#pragma unroll
+        for (int qp = 0; qp < 2; ++qp) {
+          const auto d0 = __builtin_amdgcn_permlane32_swap(X[2 * qp][0], X[2 * qp + 1][0], false, false);
+          const auto d1 = __builtin_amdgcn_permlane32_swap(X[2 * qp][1], X[2 * qp + 1][1], false, false);
+          u32x4 f;
+          f[0] = d0[0];
+          f[1] = d1[0];
+          f[2] = d0[1];
+          f[3] = d1[1];
+          const int64_t ks = ks0 + qp;
+          if (ks < n_ks)
+            __builtin_nontemporal_store(
+                f, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(E) +
+                                            frag_offset(tt, ks, wn * 4 + j, n_ks) + lane * 16));
+        }
+      }
+    }
     Sj[j] = s + __shfl_xor(s, 32, 64);
   }
   __syncthreads();  // everyone has read the maxima
@@ -305,21 +327,6 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
         pm[vt * T + t] = Mj[j];
         ps[vt * T + t] = Sj[j] + xch[(wn * 4 + j) * 32 + col];
       }
-    }
-  }
-
-  if (Store) {
-    // e (bf16, token-major rows in LDS) out with 16-byte stores of whole rows
-    __syncthreads();
-#pragma unroll 4
-    for (int c = threadIdx.x; c < kTile * 32; c += kThreads) {
-      const int tl = c >> 5;
-      const int c16 = c & 31;
-      const int64_t t = t0 + tl;
-      const int64_t v = v0 + c16 * 8;
-      if (t < T && v < Vp)
-        *reinterpret_cast<u32x4*>(E + t * Vp + v) =
-            *reinterpret_cast<const u32x4*>(lds + tl * kTrStride + c16 * 16);
     }
   }
 }
@@ -442,11 +449,12 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
 }
 
 // dhhat[t][h] = coef_t * (W[target_t][h] - sum_v p_tv W[v][h]) for a chunk,
-// with p_tv = (E[t][v] >> d(t, v / 256)) * g_t rebuilt from the stored e
+// with p_tv = (e_tv >> d(t, v / 256)) * g_t rebuilt from the stored e
 // (k_lmhead_fwd) and the shift table (shift_tables): the exponent shift is
 // applied to the A fragments inside the contraction, g_t to its result.
-// Operand A = E (token rows, K = padded vocabulary), operand B = Wt (hidden
-// rows).  The one-hot term is gathered from W exactly in fp32.
+// Operand A = E (token rows, K = padded vocabulary, in fragment order),
+// operand B = Wt (hidden rows).  The one-hot term is gathered from W exactly
+// in fp32.
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
                const float* __restrict__ gf, const uint16_t* __restrict__ Wt,
@@ -458,7 +466,7 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  GemmCoreT<true> g;
+  GemmCoreT<true, true> g;
   g.init(E, t0, TC, Wt, h0, H, Vp, lds);
   g.set_shift(D, ds, t0, (int64_t(V) + kTile - 1) / kTile);
   g.run(int(Vp));
