@@ -138,7 +138,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="qwen15b",
                     choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
-    ap.add_argument("--cpu-tokens", type=int, default=4096)
+    ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
