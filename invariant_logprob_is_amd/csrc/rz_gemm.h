@@ -365,35 +365,37 @@ struct GemmCoreT {
 
 using GemmCore = GemmCoreT<false>;
 
-// XCD-aware tile raster.  Workgroups are dealt to the 8 XCDs round-robin by
-// id; we undo that so each XCD walks a contiguous range of the logical order.
-// When the other operand has few tiles (the hidden dimension of the P*W^T
-// product: 6 tiles at H = 1536), the logical order runs all of them for a
-// token tile side by side (32 / n_other token tiles at a time), so each long
-// P row block is streamed through one XCD's L2 once.  Otherwise it visits
-// `kTokenGroup` token tiles for every tile of the other operand, so the
-// workgroups resident on one XCD share both operands in that XCD's L2.  The
-// grid is padded to a multiple of 8; returns false for the padding.
-__device__ __forceinline__ bool tile_of(int64_t n_token_tiles, int64_t n_other_tiles,
-                                        int64_t& tt, int64_t& ot) {
+// XCD-aware tile raster over an (n_a x n_b) grid of tiles.  Workgroups are
+// dealt to the 8 XCDs round-robin by id; we undo that so each XCD walks a
+// contiguous range of the logical order.  When the second dimension has few
+// tiles (the hidden dimension of the P*W^T product: 6 tiles at H = 1536), the
+// logical order runs all of them side by side for each tile of the first
+// (32 / n_b first-dimension tiles at a time), so each long operand row block
+// of the first streams through one XCD's L2 once.  Otherwise it visits
+// `kRasterGroup` tiles of the first dimension for every tile of the second:
+// the group's operand blocks stay in that XCD's L2 while the second
+// dimension's operand streams past, and the workgroups resident on one XCD
+// share both.  The grid is padded to a multiple of 8; returns false for the
+// padding.
+__device__ __forceinline__ bool tile_of(int64_t n_a, int64_t n_b, int64_t& ta, int64_t& tb) {
   const uint64_t nb = gridDim.x;
   const uint64_t b = blockIdx.x;
   const uint64_t w = (b & 7) * (nb >> 3) + (b >> 3);
-  const uint64_t no = uint64_t(n_other_tiles);
-  const uint64_t n_tiles = uint64_t(n_token_tiles) * no;
+  const uint64_t no = uint64_t(n_b);
+  const uint64_t n_tiles = uint64_t(n_a) * no;
   if (w >= n_tiles) return false;
   if (no <= 32) {
-    tt = int64_t(w / no);
-    ot = int64_t(w % no);
+    ta = int64_t(w / no);
+    tb = int64_t(w % no);
     return true;
   }
-  const uint64_t per_group = uint64_t(kTokenGroup) * no;
+  const uint64_t per_group = uint64_t(kRasterGroup) * no;
   const uint64_t g = w / per_group;
   const uint64_t rem = w - g * per_group;
-  const uint64_t left = uint64_t(n_token_tiles) - g * kTokenGroup;
-  const uint64_t gsz = left < uint64_t(kTokenGroup) ? left : uint64_t(kTokenGroup);
-  tt = int64_t(g * kTokenGroup + rem % gsz);
-  ot = int64_t(rem / gsz);
+  const uint64_t left = uint64_t(n_a) - g * kRasterGroup;
+  const uint64_t gsz = left < uint64_t(kRasterGroup) ? left : uint64_t(kRasterGroup);
+  ta = int64_t(g * kRasterGroup + rem % gsz);
+  tb = int64_t(rem / gsz);
   return true;
 }
 

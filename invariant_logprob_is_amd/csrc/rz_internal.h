@@ -17,7 +17,7 @@ constexpr int kHAlign = 64;         // H must be a multiple of this
 constexpr int kMaxH = 16384;
 constexpr int64_t kMaxV = 4000000;  // keeps a 256-row tile of the padded V below 2^31 bytes
 constexpr int64_t kBwdChunk = 32768;  // tokens per backward / learner-step chunk (bounds the P workspace)
-constexpr int kTokenGroup = 8;      // token tiles per L2 group in the tile raster
+constexpr int kRasterGroup = 8;     // first-dimension tiles per L2 group in the tile raster
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }

@@ -191,7 +191,11 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
                   float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
   __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
   int64_t tt, vt;
-  if (!tile_of(n_tt, n_vt, tt, vt)) return;
+  // Vocabulary tiles are grouped and the token tiles stream past them: the
+  // chunk's hhat (100 MB at H = 1536) stays cache-resident across the
+  // groups, where re-streaming W (467 MB) from HBM for every token group
+  // would not.
+  if (!tile_of(n_vt, n_tt, vt, tt)) return;
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
   GemmCore g;
@@ -261,7 +265,9 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
 #pragma unroll
     for (int j = 0; j < 4; ++j) xch[(wm * 8 + wn * 4 + j) * 32 + col] = Mj[j];
   }
-  __syncthreads();
+  // The exchanges below order LDS traffic only: a bare barrier, so the
+  // e stores already issued keep draining instead of being waited for.
+  GemmCore::barrier();
 #pragma unroll
   for (int j = 0; j < 4; ++j) Mj[j] = fmaxf(Mj[j], xch[((wm ^ 1) * 8 + wn * 4 + j) * 32 + col]);
 
@@ -313,12 +319,12 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
     }
     Sj[j] = s + __shfl_xor(s, 32, 64);
   }
-  __syncthreads();  // everyone has read the maxima
+  GemmCore::barrier();  // everyone has read the maxima
   if (wm == 1 && half == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) xch[(wn * 4 + j) * 32 + col] = Sj[j];
   }
-  __syncthreads();
+  GemmCore::barrier();
   if (wm == 0 && half == 0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
