@@ -36,7 +36,8 @@ import numpy as np
 
 __all__ = [
     "bf16_decode", "bf16_round", "rmsnorm", "logits", "log_softmax_gather",
-    "logprob", "advantages", "is_weights", "is_loss", "is_coef_rows", "d3", "logit_grad",
+    "logprob", "advantages", "is_weights", "is_loss", "is_coef_rows", "d3", "kl_estimators",
+    "peak_median", "decompose", "logit_grad",
     "rmsnorm_backward", "backward", "learner_step",
 ]
 
@@ -215,6 +216,51 @@ def d3(logp, mu) -> float:
     avoid cancellation when w is near 1."""
     _, delta = is_weights(logp, mu)
     return float(np.mean(np.expm1(delta) - delta))
+
+
+def kl_estimators(logp, mu):
+    """Sample estimates of the rollout-to-learner KL, KL(mu || pi), from the
+    tokens of one update, which were drawn from the rollout policy mu ([P3]
+    Fig. 1 caption: the KL is estimated from samples; [P2] "Only one
+    probability gap comes from old weights" for D3).  The pages name no
+    estimator; the reading taken is the three standard ones in the log ratio
+    delta = log pi - log mu (so w = e^delta = pi / mu):
+        k1 = mean(-delta), k2 = mean(delta^2 / 2), k3 = mean(w - 1 - delta).
+    Under tokens drawn from mu, k1 and k3 are unbiased for KL(mu || pi)
+    (E_mu[w] = 1), and k3 is the pages' D3 (same expression as d3()).  Flat
+    means over all tokens of the update.  Returns (k1, k2, k3)."""
+    _, delta = is_weights(logp, mu)
+    return (float(np.mean(-delta)), float(np.mean(0.5 * delta * delta)),
+            float(np.mean(np.expm1(delta) - delta)))
+
+
+def peak_median(series):
+    """The tracking statistic the pages report for a per-update diagnostic
+    over a training run ([P2] "Only one probability gap comes from old
+    weights" and [P3] Fig. 2: the peak of the per-update D3 over its median;
+    [P2] "Keep throughput, lag and quality conditions separate": the median
+    KL of a window of updates).  Returns (median, peak, peak / median) of the
+    values, median as numpy defines it (mean of the middle two for an even
+    count)."""
+    v = np.asarray(series, np.float64)
+    med = float(np.median(v))
+    peak = float(np.max(v))
+    return med, peak, peak / med
+
+
+def decompose(logp_learner, logp_learner_old, mu):
+    """The log-ratio decomposition of [P2] "Only one probability gap comes from
+    old weights" for one token history:
+        log pi_k - log mu_v = (log pi_k - log pi_v) + (log pi_v - log mu_v),
+    pi_k the learner at the current weights, pi_v the learner at the rollout's
+    weights, mu_v what the rollout recorded.  The first term is the weight
+    lag, the second the kernel mismatch, which batch-invariant kernels with a
+    matching forward make exactly 0 ([P3] body).  Inputs are per-token
+    log-probabilities; returns (lag, mismatch) in float64."""
+    a = np.asarray(logp_learner, np.float64)
+    b = np.asarray(logp_learner_old, np.float64)
+    m = np.asarray(mu, np.float64)
+    return a - b, b - m
 
 
 # --------------------------------------------------------------------------

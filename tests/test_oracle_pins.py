@@ -251,6 +251,60 @@ def test_d3_small_lag_noise_is_half_variance():
     assert oracle.d3(d, np.zeros_like(d)) == pytest.approx(sigma ** 2 / 2, rel=0.01)
 
 
+def test_kl_estimators_constant_delta():
+    lp = np.full(7, -3.0)
+    for c in (math.log(2.0), -0.4, 2.5):
+        k1, k2, k3 = oracle.kl_estimators(lp + c, lp)
+        assert k1 == pytest.approx(-c, rel=1e-14)
+        assert k2 == pytest.approx(c * c / 2, rel=1e-14)
+        assert k3 == pytest.approx(math.exp(c) - 1 - c, rel=1e-13)
+    assert oracle.kl_estimators(lp, lp) == (0.0, 0.0, 0.0)
+
+
+def test_kl_estimators_k1_k3_equal_kl_by_enumeration():
+    # tokens drawn from mu with exact multiplicities: E_mu[-log(pi/mu)] and
+    # E_mu[pi/mu - 1 - log(pi/mu)] both equal KL(mu || pi); k2 does not
+    from scipy.stats import entropy
+    counts = np.array([3, 1, 4, 1, 5, 9, 2, 6])
+    mu = counts / counts.sum()
+    pi = np.array([0.05, 0.2, 0.1, 0.15, 0.1, 0.2, 0.1, 0.1])
+    tok = np.repeat(np.arange(len(counts)), counts)
+    k1, k2, k3 = oracle.kl_estimators(np.log(pi[tok]), np.log(mu[tok]))
+    kl = entropy(mu, pi)
+    assert k1 == pytest.approx(kl, rel=1e-13)
+    assert k3 == pytest.approx(kl, rel=1e-13)
+    assert abs(k2 - kl) > 1e-3 * kl
+
+
+def test_kl_estimators_small_noise_limit():
+    rng = np.random.default_rng(5)
+    sigma = 0.02
+    d = rng.normal(0, sigma, 1_000_000)
+    k1, k2, k3 = oracle.kl_estimators(d, np.zeros_like(d))
+    assert abs(k1) < 5 * sigma / 1000
+    assert k2 == pytest.approx(sigma ** 2 / 2, rel=0.01)
+    assert k3 == pytest.approx(sigma ** 2 / 2, rel=0.01)
+
+
+def test_peak_median_hand_values():
+    assert oracle.peak_median([1.0, 2.0, 3.0, 10.0]) == (2.5, 10.0, 4.0)
+    assert oracle.peak_median([3.0, 1.0, 2.0]) == (2.0, 3.0, 1.5)
+    assert oracle.peak_median([0.5]) == (0.5, 0.5, 1.0)
+
+
+def test_decompose_identity_and_degenerate_cases():
+    rng = np.random.default_rng(6)
+    a, b, m = rng.normal(-3, 1, (3, 50))
+    lag, mis = oracle.decompose(a, b, m)
+    np.testing.assert_allclose(lag + mis, a - m, rtol=0, atol=1e-14)
+    np.testing.assert_array_equal(lag, a - b)
+    # same weights: no lag; rollout recorded the learner's own values: no mismatch
+    lag0, _ = oracle.decompose(b, b, m)
+    assert np.all(lag0 == 0.0)
+    _, mis0 = oracle.decompose(a, b, b)
+    assert np.all(mis0 == 0.0)
+
+
 # ---------------------------------------------------------------- backward
 
 def _chain_loss(xv, gv, eps, Wv, tgt, mu, ro, go, reward):
