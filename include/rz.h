@@ -145,6 +145,48 @@ int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
           double* d3, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rz_kl -- sample estimates of the rollout-to-learner KL, KL(mu || pi), over
+ * the tokens of one update ([P3] Fig. 1 caption: a KL estimated from the
+ * rollout's samples; the pages name no estimator).  With delta = logprob -
+ * rollout_logprob:
+ *   kl[0] = k1 = (1/T) sum_t (-delta_t),
+ *   kl[1] = k2 = (1/T) sum_t delta_t^2 / 2,
+ *   kl[2] = k3 = (1/T) sum_t (expm1(delta_t) - delta_t)   (= rz_d3's value,
+ *                                                           bit for bit),
+ * fp64 with a fixed order.  k1 and k3 are unbiased for KL(mu || pi) when the
+ * tokens were drawn from mu.  Output kl [3] fp64 (device).
+ * Errors: RZ_EINVAL (null pointer, T < 1), RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
+ */
+int rz_kl(const float* logprob, const float* rollout_logprob, int64_t T,
+          double* kl, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_decompose -- the log-ratio decomposition of [P2] "Only one probability
+ * gap comes from old weights", token by token:
+ *   log pi_new - log mu = (log pi_new - log pi_old) + (log pi_old - log mu),
+ * lag[t] = the first term (weight lag), mismatch[t] = the second (kernel
+ * mismatch): pi_new and pi_old are this library's log-probabilities at the
+ * learner's current head (x_new, gamma_new, W_new) and at the rollout's
+ * (x_old, gamma_old, W_old), for the same targets, and mu is what the rollout
+ * recorded.  When mu came from this library's rz_logprob at the rollout's
+ * weights, in any batching, the mismatch is exactly 0 for every token (the
+ * pages' claim, checked token by token).
+ * Each difference is exact in fp64 and rounded once to fp32.
+ * summary [4] fp64: max |lag|, mean lag, max |mismatch|, and the number of
+ * tokens whose mismatch is not exactly 0 (NaN counts).
+ * x_*, gamma_*, W_*, eps, target, T, H, V as for rz_logprob (both versions
+ * share the shape); rollout_logprob [T] fp32; lag, mismatch [T] fp32 out
+ * (distinct, and distinct from rollout_logprob); workspace as rz_logprob.
+ * Errors: as rz_logprob.
+ */
+int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_t* W_new,
+                 const uint16_t* x_old, const uint16_t* gamma_old, const uint16_t* W_old,
+                 float eps, const int32_t* target, const float* rollout_logprob,
+                 int64_t T, int32_t H, int32_t V,
+                 float* lag, float* mismatch, double* summary,
+                 void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rz_backward -- gradient of the loss with respect to the pre-norm hidden
  * states, given lse (from rz_logprob) and coef (from rz_is_loss).
  *
@@ -188,7 +230,8 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
  *
  * Arguments as for rz_logprob, rz_is_loss, rz_d3 and rz_backward.  Outputs:
  * logprob [T] fp32; lse [T] fp32 (may be NULL); loss [1] fp64; d3 [1] fp64;
- * coef [T] fp32 (may be NULL); dhidden [T,H] fp32.
+ * kl [3] fp64 (may be NULL; as rz_kl); coef [T] fp32 (may be NULL);
+ * dhidden [T,H] fp32.
  * Errors: the union of those of rz_logprob and rz_is_loss.
  */
 int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
@@ -197,7 +240,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
                     const int64_t* resp_offsets, int32_t R,
                     const int64_t* group_offsets, int32_t G,
                     const float* reward,
-                    float* logprob, float* lse, double* loss, double* d3,
+                    float* logprob, float* lse, double* loss, double* d3, double* kl,
                     float* coef, float* dhidden,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -20,8 +20,9 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RzError", "lib", "version", "workspace_bytes", "logprob", "is_loss", "d3",
-    "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH", "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
+    "RzError", "lib", "version", "workspace_bytes", "logprob", "is_loss", "d3", "kl",
+    "decompose", "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH",
+    "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
 ]
 
@@ -44,8 +45,11 @@ SYMBOLS = {
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_backward": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "rz_kl": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
+    "rz_decompose": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P,
+                                    _P, _P, _SZ, _P]),
     "rz_learner_step": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _P, _I32, _P,
-                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "rz_profile_count": (ctypes.c_int, []),
     "rz_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -229,6 +233,58 @@ def d3(logprob, rollout_logprob, *, workspace=None):
     return out
 
 
+def kl(logprob, rollout_logprob, *, workspace=None):
+    """KL estimators (rz_kl): (k1, k2, k3) = token means of -delta,
+    delta^2/2 and expm1(delta) - delta.  Returns [3] fp64."""
+    torch = _torch()
+    dev = logprob.device
+    _need(logprob, "logprob", torch.float32, dev, 1)
+    _need(rollout_logprob, "rollout_logprob", torch.float32, dev, 1)
+    T = logprob.shape[0]
+    if rollout_logprob.shape[0] != T:
+        raise ValueError("logprob and rollout_logprob differ in length")
+    out = torch.empty(3, dtype=torch.float64, device=dev)
+    ws = _workspace(workspace_bytes(T, 64, 1), dev, workspace)
+    st = lib().rz_kl(logprob.data_ptr(), rollout_logprob.data_ptr(), T, out.data_ptr(),
+                     ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_kl", st)
+    return out
+
+
+def decompose(x_new, gamma_new, W_new, x_old, gamma_old, W_old, target, rollout_logprob,
+              eps: float = 1e-6, *, workspace=None):
+    """Token-level log-ratio decomposition (rz_decompose).  Returns a dict
+    with lag, mismatch [T] fp32 and summary [4] fp64 (max |lag|, mean lag,
+    max |mismatch|, tokens with mismatch != 0)."""
+    torch = _torch()
+    dev = x_new.device
+    _need(x_new, "x_new", torch.bfloat16, dev, 2)
+    T, H = x_new.shape
+    _need(x_old, "x_old", torch.bfloat16, dev, 2)
+    for n, g in (("gamma_new", gamma_new), ("gamma_old", gamma_old)):
+        _need(g, n, torch.bfloat16, dev, 1)
+    for n, w in (("W_new", W_new), ("W_old", W_old)):
+        _need(w, n, torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    _need(rollout_logprob, "rollout_logprob", torch.float32, dev, 1)
+    V = W_new.shape[0]
+    if (tuple(x_old.shape) != (T, H) or gamma_new.shape[0] != H or gamma_old.shape[0] != H
+            or tuple(W_new.shape) != (V, H) or tuple(W_old.shape) != (V, H)
+            or target.shape[0] != T or rollout_logprob.shape[0] != T):
+        raise ValueError("shape mismatch among decompose arguments")
+    lag = torch.empty(T, dtype=torch.float32, device=dev)
+    mis = torch.empty(T, dtype=torch.float32, device=dev)
+    summary = torch.empty(4, dtype=torch.float64, device=dev)
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    st = lib().rz_decompose(x_new.data_ptr(), gamma_new.data_ptr(), W_new.data_ptr(),
+                            x_old.data_ptr(), gamma_old.data_ptr(), W_old.data_ptr(), float(eps),
+                            target.data_ptr(), rollout_logprob.data_ptr(), T, H, V,
+                            lag.data_ptr(), mis.data_ptr(), summary.data_ptr(), ws.data_ptr(),
+                            ws.numel(), _stream(dev))
+    _check("rz_decompose", st)
+    return {"lag": lag, "mismatch": mis, "summary": summary}
+
+
 def backward(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, workspace=None, out=None):
     """Gradient of the loss with respect to the pre-norm hidden states
     (rz_backward).  Returns dhidden [T,H] fp32."""
@@ -261,8 +317,8 @@ def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offse
     log-probabilities (bit-identical to logprob()), the IS loss, D3, the
     per-token loss gradient coef and dhidden, computing the logits once.
 
-    Returns a dict with logprob, lse, coef [T] fp32, loss, d3 [1] fp64 and
-    dhidden [T,H] fp32.  `out` may supply preallocated tensors for any of
+    Returns a dict with logprob, lse, coef [T] fp32, loss, d3 [1] fp64,
+    kl [3] fp64 (k1, k2, k3 as kl()) and dhidden [T,H] fp32.  `out` may supply preallocated tensors for any of
     these keys."""
     torch = _torch()
     dev = x.device
@@ -288,7 +344,8 @@ def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offse
     o = dict(out or {})
     specs = {"logprob": ((T,), torch.float32), "lse": ((T,), torch.float32),
              "coef": ((T,), torch.float32), "loss": ((1,), torch.float64),
-             "d3": ((1,), torch.float64), "dhidden": ((T, H), torch.float32)}
+             "d3": ((1,), torch.float64), "kl": ((3,), torch.float64),
+             "dhidden": ((T, H), torch.float32)}
     for k, (shape, dt) in specs.items():
         if k not in o:
             o[k] = torch.empty(shape, dtype=dt, device=dev)
@@ -298,7 +355,8 @@ def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offse
                                target.data_ptr(), rollout_logprob.data_ptr(), T, H, V,
                                ro.data_ptr(), R, go.data_ptr(), G, rw.data_ptr(),
                                o["logprob"].data_ptr(), o["lse"].data_ptr(), o["loss"].data_ptr(),
-                               o["d3"].data_ptr(), o["coef"].data_ptr(), o["dhidden"].data_ptr(),
+                               o["d3"].data_ptr(), o["kl"].data_ptr(), o["coef"].data_ptr(),
+                               o["dhidden"].data_ptr(),
                                ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_learner_step", st)
     return o

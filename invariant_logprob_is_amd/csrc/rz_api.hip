@@ -36,6 +36,22 @@ T_* at(void* ws, size_t off) {
   return reinterpret_cast<T_*>(static_cast<char*>(ws) + off);
 }
 
+// a1-a3 for rz_logprob and rz_decompose (arguments already checked).
+hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                       const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
+                       float* lse, void* workspace, const WsLayout& L, hipStream_t s) {
+  uint16_t* hhat = at<uint16_t>(workspace, L.hhat);
+  float* pm = at<float>(workspace, L.pm);
+  float* ps = at<float>(workspace, L.ps);
+  float* zt = at<float>(workspace, L.ztgt);
+  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
+  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, nullptr, s);
+  if (e == hipSuccess)
+    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, nullptr, 0,
+                           nullptr, s);
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -74,17 +90,8 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
   st = check_device();
   if (st != RZ_OK) return st;
 
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* hhat = at<uint16_t>(workspace, L.hhat);
-  float* pm = at<float>(workspace, L.pm);
-  float* ps = at<float>(workspace, L.ps);
-  float* zt = at<float>(workspace, L.ztgt);
-  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
-  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, nullptr, s);
-  if (e == hipSuccess)
-    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, nullptr, 0,
-                           nullptr, s);
-  return status_of(e);
+  return status_of(run_logprob(x, gamma, eps, W, target, T, H, V, logprob, lse, workspace, L,
+                               static_cast<hipStream_t>(stream)));
 }
 
 int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
@@ -122,6 +129,56 @@ int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T, double*
   if (st != RZ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(launch_d3(logprob, rollout_logprob, T, d3, at<double>(workspace, L.part), s));
+}
+
+int rz_kl(const float* logprob, const float* rollout_logprob, int64_t T, double* kl,
+          void* workspace, size_t workspace_bytes, void* stream) {
+  if (!logprob || !rollout_logprob || !kl || !workspace) return RZ_EINVAL;
+  if (!aligned4(logprob) || !aligned4(rollout_logprob) || !aligned8(kl) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (T < 1) return RZ_EINVAL;
+  const WsLayout L = ws_layout(T, 64, 1);
+  if (workspace_bytes < L.loss_end) return RZ_EWORKSPACE;
+  const int st = check_device();
+  if (st != RZ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  return status_of(launch_kl(logprob, rollout_logprob, T, kl, at<double>(workspace, L.part), s));
+}
+
+int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_t* W_new,
+                 const uint16_t* x_old, const uint16_t* gamma_old, const uint16_t* W_old,
+                 float eps, const int32_t* target, const float* rollout_logprob, int64_t T,
+                 int32_t H, int32_t V, float* lag, float* mismatch, double* summary,
+                 void* workspace, size_t workspace_bytes, void* stream) {
+  if (!x_new || !gamma_new || !W_new || !x_old || !gamma_old || !W_old || !target ||
+      !rollout_logprob || !lag || !mismatch || !summary || !workspace)
+    return RZ_EINVAL;
+  if (!aligned16(x_new) || !aligned16(gamma_new) || !aligned16(W_new) || !aligned16(x_old) ||
+      !aligned16(gamma_old) || !aligned16(W_old) || !aligned4(target) ||
+      !aligned4(rollout_logprob) || !aligned4(lag) || !aligned4(mismatch) || !aligned8(summary) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (lag == mismatch || rollout_logprob == lag || rollout_logprob == mismatch) return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  const WsLayout L = ws_layout(T, H, V);
+  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the two log-probabilities go straight into the output arrays; the last
+  // kernel turns them into (lag, mismatch) in place
+  hipError_t e = run_logprob(x_new, gamma_new, eps, W_new, target, T, H, V, lag, nullptr,
+                             workspace, L, s);
+  if (e == hipSuccess)
+    e = run_logprob(x_old, gamma_old, eps, W_old, target, T, H, V, mismatch, nullptr, workspace,
+                    L, s);
+  if (e == hipSuccess)
+    e = launch_decompose(lag, mismatch, rollout_logprob, T, lag, mismatch, summary,
+                         at<double>(workspace, L.part), s);
+  return status_of(e);
 }
 
 int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
@@ -169,7 +226,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
                     const int32_t* target, const float* rollout_logprob, int64_t T, int32_t H,
                     int32_t V, const int64_t* resp_offsets, int32_t R,
                     const int64_t* group_offsets, int32_t G, const float* reward, float* logprob,
-                    float* lse, double* loss, double* d3, float* coef, float* dhidden,
+                    float* lse, double* loss, double* d3, double* kl, float* coef, float* dhidden,
                     void* workspace, size_t workspace_bytes, void* stream) {
   if (!x || !gamma || !W || !target || !rollout_logprob || !resp_offsets || !group_offsets ||
       !reward || !logprob || !loss || !d3 || !dhidden || !workspace)
@@ -177,7 +234,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
   if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) ||
       !aligned4(rollout_logprob) || !aligned8(resp_offsets) || !aligned8(group_offsets) ||
       !aligned4(reward) || !aligned4(logprob) || (lse && !aligned4(lse)) || !aligned8(loss) ||
-      !aligned8(d3) || (coef && !aligned4(coef)) || !aligned16(dhidden) ||
+      !aligned8(d3) || (kl && !aligned8(kl)) || (coef && !aligned4(coef)) || !aligned16(dhidden) ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return RZ_EINVAL;
   if (!(eps >= 0.0f)) return RZ_EINVAL;
@@ -223,6 +280,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     e = launch_is_loss(logprob, rollout_logprob, T, resp_offsets, R, group_offsets, G, reward,
                        loss, nullptr, nullptr, part, s);
   if (e == hipSuccess) e = launch_d3(logprob, rollout_logprob, T, d3, part, s);
+  if (e == hipSuccess && kl) e = launch_kl(logprob, rollout_logprob, T, kl, part, s);
   return status_of(e);
 }
 

@@ -67,7 +67,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.b_g = o;    o = align256(o + size_t(tc) * 4);
   L.bwd_end = o;
   o = 0;
-  L.part = o;   o = align256(o + size_t(T + 1) * 8);
+  L.part = o;   o = align256(o + size_t(T + 8) * 8);
   L.loss_end = o;
   o = 0;
   L.s_hhat = o; o = align256(o + size_t(tc) * H * 2);
@@ -81,7 +81,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.s_cs = o;   o = align256(o + size_t(T) * 8);
   L.s_lse = o;  o = align256(o + size_t(T) * 4);
   L.s_coef = o; o = align256(o + size_t(T) * 4);
-  L.s_part = o; o = align256(o + size_t(T + 1) * 8);
+  L.s_part = o; o = align256(o + size_t(T + 8) * 8);
   L.step_end = o;
   L.total = L.fwd_end;
   if (L.bwd_end > L.total) L.total = L.bwd_end;
@@ -140,5 +140,10 @@ hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T,
                           double* part, hipStream_t s);
 hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3,
                      double* part, hipStream_t s);
+hipError_t launch_kl(const float* logprob, const float* mu, int64_t T, double* kl,
+                     double* part, hipStream_t s);
+hipError_t launch_decompose(const float* lp_new, const float* lp_old, const float* mu, int64_t T,
+                            float* lag, float* mismatch, double* summary, double* part,
+                            hipStream_t s);
 
 }  // namespace rz

@@ -572,6 +572,20 @@ __device__ __forceinline__ double block_sum_256(double v, double* sh) {
   return r;
 }
 
+__device__ __forceinline__ double block_max_256(double v, double* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+#pragma unroll
+  for (int w = 128; w >= 1; w >>= 1) {
+    if (tid < w) sh[tid] = fmax(sh[tid], sh[tid + w]);
+    __syncthreads();
+  }
+  const double r = sh[0];
+  __syncthreads();
+  return r;
+}
+
 // One workgroup per response i.
 __global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logprob,
                                                  const float* __restrict__ mu, int64_t T,
@@ -629,28 +643,114 @@ __global__ __launch_bounds__(256) void k_is_final(const double* __restrict__ par
 
 constexpr int64_t kD3Block = 16384;
 
-__global__ __launch_bounds__(256) void k_d3_part(const float* __restrict__ logprob,
+// The three KL estimators over one update's tokens, delta = logprob - mu:
+// per block of kD3Block tokens the partial sums of -delta, delta^2 / 2 and
+// expm1(delta) - delta (float64, a fixed in-block tree), then one block sums
+// the partials in block order.  D3 is the third of them; rz_d3 runs the same
+// kernels, so its bits equal k3's.
+__global__ __launch_bounds__(256) void k_kl_part(const float* __restrict__ logprob,
                                                  const float* __restrict__ mu, int64_t T,
                                                  double* __restrict__ part) {
   __shared__ double sh[256];
   const int64_t a = int64_t(blockIdx.x) * kD3Block;
   const int64_t b = a + kD3Block < T ? a + kD3Block : T;
-  double s = 0.0;
+  double s1 = 0.0, s2 = 0.0, s3 = 0.0;
   for (int64_t t = a + threadIdx.x; t < b; t += 256) {
     const double d = double(logprob[t]) - double(mu[t]);
-    s += expm1(d) - d;
+    s1 -= d;
+    s2 += 0.5 * d * d;
+    s3 += expm1(d) - d;
   }
-  s = block_sum_256(s, sh);
-  if (threadIdx.x == 0) part[blockIdx.x] = s;
+  s1 = block_sum_256(s1, sh);
+  s2 = block_sum_256(s2, sh);
+  s3 = block_sum_256(s3, sh);
+  if (threadIdx.x == 0) {
+    part[3 * blockIdx.x] = s1;
+    part[3 * blockIdx.x + 1] = s2;
+    part[3 * blockIdx.x + 2] = s3;
+  }
 }
 
-__global__ __launch_bounds__(256) void k_d3_final(const double* __restrict__ part, int64_t nb,
-                                                  int64_t T, double* __restrict__ d3) {
+// out[0..2] = (k1, k2, k3), or with only_k3 out[0] = k3.
+__global__ __launch_bounds__(256) void k_kl_final(const double* __restrict__ part, int64_t nb,
+                                                  int64_t T, int only_k3,
+                                                  double* __restrict__ out) {
   __shared__ double sh[256];
-  double s = 0.0;
-  for (int64_t i = threadIdx.x; i < nb; i += 256) s += part[i];
-  s = block_sum_256(s, sh);
-  if (threadIdx.x == 0) *d3 = s / double(T);
+  double k[3];
+#pragma unroll
+  for (int q = 0; q < 3; ++q) {
+    double s = 0.0;
+    for (int64_t i = threadIdx.x; i < nb; i += 256) s += part[3 * i + q];
+    k[q] = block_sum_256(s, sh) / double(T);
+  }
+  if (threadIdx.x == 0) {
+    if (only_k3) {
+      out[0] = k[2];
+    } else {
+      out[0] = k[0];
+      out[1] = k[1];
+      out[2] = k[2];
+    }
+  }
+}
+
+// The log-ratio decomposition per token: lag = lp_new - lp_old and mismatch =
+// lp_old - mu (each difference exact in float64, then rounded once), and per
+// block of kD3Block tokens: max |lag|, sum lag, max |mismatch| and the count
+// of tokens whose mismatch is not exactly 0 (NaN counts).  lag and mismatch
+// may alias lp_new and lp_old.
+__global__ __launch_bounds__(256) void k_decompose(const float* lp_new, const float* lp_old,
+                                                   const float* __restrict__ mu, int64_t T,
+                                                   float* lag, float* mismatch,
+                                                   double* __restrict__ part) {
+  __shared__ double sh[256];
+  const int64_t a = int64_t(blockIdx.x) * kD3Block;
+  const int64_t b = a + kD3Block < T ? a + kD3Block : T;
+  double mx_lag = 0.0, sum_lag = 0.0, mx_mis = 0.0, n_mis = 0.0;
+  for (int64_t t = a + threadIdx.x; t < b; t += 256) {
+    const double pn = double(lp_new[t]), po = double(lp_old[t]), m = double(mu[t]);
+    const double l = pn - po, d = po - m;
+    lag[t] = float(l);
+    mismatch[t] = float(d);
+    mx_lag = fmax(mx_lag, fabs(l));
+    sum_lag += l;
+    mx_mis = fmax(mx_mis, fabs(d));
+    n_mis += (d == 0.0) ? 0.0 : 1.0;
+  }
+  mx_lag = block_max_256(mx_lag, sh);
+  sum_lag = block_sum_256(sum_lag, sh);
+  mx_mis = block_max_256(mx_mis, sh);
+  n_mis = block_sum_256(n_mis, sh);
+  if (threadIdx.x == 0) {
+    part[4 * blockIdx.x] = mx_lag;
+    part[4 * blockIdx.x + 1] = sum_lag;
+    part[4 * blockIdx.x + 2] = mx_mis;
+    part[4 * blockIdx.x + 3] = n_mis;
+  }
+}
+
+// summary = (max |lag|, mean lag, max |mismatch|, tokens with mismatch != 0).
+__global__ __launch_bounds__(256) void k_decompose_final(const double* __restrict__ part,
+                                                         int64_t nb, int64_t T,
+                                                         double* __restrict__ summary) {
+  __shared__ double sh[256];
+  double v[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t i = threadIdx.x; i < nb; i += 256) {
+    v[0] = fmax(v[0], part[4 * i]);
+    v[1] += part[4 * i + 1];
+    v[2] = fmax(v[2], part[4 * i + 2]);
+    v[3] += part[4 * i + 3];
+  }
+  v[0] = block_max_256(v[0], sh);
+  v[1] = block_sum_256(v[1], sh);
+  v[2] = block_max_256(v[2], sh);
+  v[3] = block_sum_256(v[3], sh);
+  if (threadIdx.x == 0) {
+    summary[0] = v[0];
+    summary[1] = v[1] / double(T);
+    summary[2] = v[2];
+    summary[3] = v[3];
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -748,10 +848,30 @@ hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T, cons
 
 hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3, double* part,
                      hipStream_t s) {
-  ProfScope prof("k_d3", s);
+  ProfScope prof("k_kl", s);
   const int64_t nb = ceil_div(T, kD3Block);
-  hipLaunchKernelGGL(k_d3_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
-  hipLaunchKernelGGL(k_d3_final, dim3(1), dim3(256), 0, s, part, nb, T, d3);
+  hipLaunchKernelGGL(k_kl_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
+  hipLaunchKernelGGL(k_kl_final, dim3(1), dim3(256), 0, s, part, nb, T, 1, d3);
+  return hipGetLastError();
+}
+
+hipError_t launch_kl(const float* logprob, const float* mu, int64_t T, double* kl, double* part,
+                     hipStream_t s) {
+  ProfScope prof("k_kl", s);
+  const int64_t nb = ceil_div(T, kD3Block);
+  hipLaunchKernelGGL(k_kl_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
+  hipLaunchKernelGGL(k_kl_final, dim3(1), dim3(256), 0, s, part, nb, T, 0, kl);
+  return hipGetLastError();
+}
+
+hipError_t launch_decompose(const float* lp_new, const float* lp_old, const float* mu, int64_t T,
+                            float* lag, float* mismatch, double* summary, double* part,
+                            hipStream_t s) {
+  ProfScope prof("k_decompose", s);
+  const int64_t nb = ceil_div(T, kD3Block);
+  hipLaunchKernelGGL(k_decompose, dim3(uint32_t(nb)), dim3(256), 0, s, lp_new, lp_old, mu, T, lag,
+                     mismatch, part);
+  hipLaunchKernelGGL(k_decompose_final, dim3(1), dim3(256), 0, s, part, nb, T, summary);
   return hipGetLastError();
 }
 

@@ -137,15 +137,48 @@ def test_d3_argument_validation():
     assert L.rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 8, None) == rz.RZ_EWORKSPACE
 
 
+def test_kl_argument_validation():
+    L = rz.lib()
+    assert L.rz_kl(None, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_kl(FAKE, None, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_kl(FAKE, FAKE, 10, None, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_kl(FAKE, FAKE, 0, FAKE, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_kl(FAKE, FAKE, 10, FAKE + 4, FAKE, 1 << 20, None) == rz.RZ_EINVAL
+    assert L.rz_kl(FAKE, FAKE, 10, FAKE, FAKE, 8, None) == rz.RZ_EWORKSPACE
+
+
+def _dec(**kw):
+    a = dict(xn=FAKE, gn=FAKE, Wn=FAKE, xo=FAKE, go=FAKE, Wo=FAKE, eps=1e-6, target=FAKE,
+             mu=FAKE + 4096, T=300, H=128, V=1024, lag=FAKE + 8192, mis=FAKE + 16384,
+             summ=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_decompose(a["xn"], a["gn"], a["Wn"], a["xo"], a["go"], a["Wo"], a["eps"],
+                                 a["target"], a["mu"], a["T"], a["H"], a["V"], a["lag"],
+                                 a["mis"], a["summ"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decompose_argument_validation():
+    for k in ("xn", "gn", "Wn", "xo", "go", "Wo", "target", "mu", "lag", "mis", "summ", "ws"):
+        assert _dec(**{k: None}) == rz.RZ_EINVAL, k
+    assert _dec(xo=FAKE + 8) == rz.RZ_EINVAL
+    assert _dec(summ=FAKE + 4) == rz.RZ_EINVAL
+    assert _dec(mis=FAKE + 8192) == rz.RZ_EINVAL      # lag and mismatch must differ
+    assert _dec(mu=FAKE + 8192) == rz.RZ_EINVAL       # mu may not alias an output
+    assert _dec(T=0) == rz.RZ_EINVAL
+    assert _dec(eps=-1.0) == rz.RZ_EINVAL
+    assert _dec(H=96) == rz.RZ_EUNSUPPORTED
+    assert _dec(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
+
+
 def _step(**kw):
     a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, mu=FAKE, T=300, H=128, V=1024,
              ro=FAKE, R=16, go=FAKE, G=4, reward=FAKE, lp=FAKE, lse=FAKE, loss=FAKE, d3=FAKE,
-             coef=FAKE, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+             kl=FAKE, coef=FAKE, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
     return rz.lib().rz_learner_step(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["mu"],
                                     a["T"], a["H"], a["V"], a["ro"], a["R"], a["go"], a["G"],
-                                    a["reward"], a["lp"], a["lse"], a["loss"], a["d3"], a["coef"],
-                                    a["dh"], a["ws"], a["wsb"], a["stream"])
+                                    a["reward"], a["lp"], a["lse"], a["loss"], a["d3"], a["kl"],
+                                    a["coef"], a["dh"], a["ws"], a["wsb"], a["stream"])
 
 
 def test_learner_step_argument_validation():
@@ -153,6 +186,7 @@ def test_learner_step_argument_validation():
         assert _step(**{k: None}) == rz.RZ_EINVAL, k
     assert _step(x=FAKE + 8) == rz.RZ_EINVAL
     assert _step(dh=FAKE + 4) == rz.RZ_EINVAL
+    assert _step(kl=FAKE + 4) == rz.RZ_EINVAL      # fp64 output needs 8-byte alignment
     assert _step(ro=FAKE + 4) == rz.RZ_EINVAL
     assert _step(T=0) == rz.RZ_EINVAL
     assert _step(R=0) == rz.RZ_EINVAL

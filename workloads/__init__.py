@@ -26,7 +26,7 @@ ROW_BLOCK = 65536
 # Child indices of the master SeedSequence (fixed forever: changing one changes
 # the data of every config).
 _C_LENGTHS, _C_X, _C_GAMMA, _C_W, _C_TARGET, _C_NOISE, _C_REWARD, _C_TAILS, \
-    _C_OUTLIERS, _C_FILLER, _C_PLACEMENT = range(11)
+    _C_OUTLIERS, _C_FILLER, _C_PLACEMENT, _C_VERSION = range(12)
 _N_CHILDREN = 16
 
 
@@ -254,6 +254,29 @@ def compose_batch(sweep: InvarianceSweep, ids: np.ndarray, pos: np.ndarray, B: i
     x[pos] = sweep.fixed_x[ids]
     t[pos] = sweep.fixed_target[ids]
     return x, t
+
+
+def older_version(master: int, x_bits: np.ndarray, gamma_bits: np.ndarray, W_bits: np.ndarray,
+                  w_sigma: float, x_sigma: float = 0.0, gamma_sigma: float = 0.0):
+    """The head at an older weight version, for the log-ratio decomposition:
+    every element of W (and of x, gamma when their sigma is not 0) moved by
+    an independent N(0, sigma) draw and rounded to bf16 again.  Draws come
+    from the config's own stream (master seed, version child); W is drawn in
+    ROW_BLOCK row blocks like the other tensors.  Returns (x, gamma, W) bits."""
+    rng = _rng(master, _C_VERSION)
+
+    def moved(bits, sigma):
+        if sigma == 0.0:
+            return bits
+        a = bits.reshape(-1, bits.shape[-1]) if bits.ndim > 1 else bits.reshape(1, -1)
+        out = np.empty_like(a)
+        for r0 in range(0, a.shape[0], ROW_BLOCK):
+            r1 = min(a.shape[0], r0 + ROW_BLOCK)
+            d = rng.standard_normal((r1 - r0, a.shape[1]), dtype=np.float32) * np.float32(sigma)
+            out[r0:r1] = f32_to_bf16_bits(bf16_bits_to_f32(a[r0:r1]) + d)
+        return out.reshape(bits.shape)
+
+    return moved(x_bits, x_sigma), moved(gamma_bits, gamma_sigma), moved(W_bits, w_sigma)
 
 
 CONFIGS = {
