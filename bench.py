@@ -131,6 +131,80 @@ def summarize_counters(fetch_csv: str, write_csv: str):
               f"(factors {cf:.3f}, {cw:.3f})")
 
 
+def probe(args, b, rz, x, g, W, tgt, lp, ws, stream):
+    """The decomposition probe on the same workload: the rollout's weights are
+    an older version of the head (every gamma and W element moved by
+    N(0, 1e-3)), mu is recorded at those weights in another batching
+    (8191-row calls), and rz_decompose splits log pi - log mu per token.
+    Then the KL estimators are tracked over 16 synthetic updates."""
+    import torch
+    import workloads
+    from invariant_logprob_is_amd.tracking import UpdateTracker
+
+    dev = x.device
+    _, g_old, W_old = workloads.older_version(1, b.x[:1], b.gamma, b.W, 1e-3, 0.0, 1e-3)
+    go = torch.from_numpy(g_old.view(np.int16)).view(torch.bfloat16).to(dev)
+    Wo = torch.from_numpy(np.ascontiguousarray(W_old).view(np.int16)).view(torch.bfloat16).to(dev)
+    T, H, V = b.T, b.H, b.V
+    mu = torch.empty(T, dtype=torch.float32, device=dev)
+    for a in range(0, T, 8191):
+        c = min(T, a + 8191)
+        mu[a:c] = rz.logprob(x[a:c], go, Wo, tgt[a:c], b.eps, workspace=ws)[0]
+    torch.cuda.synchronize()
+
+    def call():
+        return rz.decompose(x, g, W, x, go, Wo, tgt, mu, b.eps, workspace=ws)
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    rz.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = rz.profile_read()
+    rz.profile_enable(False)
+    ms = 1000.0 * wall / args.steps
+    summ = out["summary"].cpu().numpy()
+    log(f"probe {ms:.2f} ms/call; max|lag|={summ[0]:.3e} mean lag={summ[1]:.3e} "
+        f"max|mismatch|={summ[2]:.3e} tokens with mismatch={int(summ[3])}")
+    for k, (tot, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        log(f"  {k:16s} {tot / args.steps:9.3f} ms/call  {n // args.steps:4d} launches/call")
+    tot, n = prof["k_lmhead_fwd"]
+    achieved = 2 * 2.0 * T * H * V * args.steps / (tot / 1000.0)
+
+    # KL tracking over synthetic updates: mu_u = logprob + sigma_u * (a seeded
+    # permutation of the workload's N(0, 1) lag noise), sigma_u ~ lognormal
+    # around 0.05, one update with a tenfold spike
+    rng = np.random.default_rng(20260)
+    base = b.lag_noise / np.float32(b.lag_noise.std())
+    sig = 0.05 * np.exp(rng.normal(0, 0.2, 16))
+    sig[11] *= 10.0
+    tr = UpdateTracker()
+    for u in range(16):
+        noise = torch.from_numpy((base[rng.permutation(T)] * np.float32(sig[u])).astype(np.float32))
+        tr.add(rz.kl(lp, (lp + noise.to(dev)).contiguous(), workspace=ws))
+    track = tr.summary()
+    log(f"kl tracking over 16 updates: D3 median {track['k3']['median']:.3e}, "
+        f"peak/median {track['k3']['peak_over_median']:.2f}")
+    print(json.dumps({
+        "metric": "decomposition probe tokens/sec (two forward passes + per-token lag/mismatch split), 1 GPU",
+        "value": T / (ms / 1000.0), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}; rollout weights moved by N(0, 1e-3)",
+                   "T": T, "H": H, "V": V},
+        "summary": {"max_abs_lag": float(summ[0]), "mean_lag": float(summ[1]),
+                    "max_abs_mismatch": float(summ[2]), "tokens_with_mismatch": int(summ[3])},
+        "kl_tracking": track,
+        "roofline": {"kernel": "k_lmhead_fwd", "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -140,6 +214,9 @@ def main():
                     choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--probe", action="store_true",
+                    help="time the log-ratio decomposition probe (rz_decompose) and track the KL "
+                         "estimators over synthetic updates instead of the learner step")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/traffic_<kernel>.json and exit")
@@ -193,6 +270,9 @@ def main():
     torch.empty_like(cal).copy_(cal)
     del cal
     torch.cuda.synchronize()
+    if args.probe:
+        probe(args, b, rz, x, g, W, tgt, lp, ws, stream)
+        return
 
     def step():
         rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs)

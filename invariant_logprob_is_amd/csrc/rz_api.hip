@@ -36,7 +36,10 @@ T_* at(void* ws, size_t off) {
   return reinterpret_cast<T_*>(static_cast<char*>(ws) + off);
 }
 
-// a1-a3 for rz_logprob and rz_decompose (arguments already checked).
+// a1-a3 for rz_logprob and rz_decompose (arguments already checked), in
+// chunks of at most kBwdChunk tokens: a chunk's hhat (100 MB at H = 1536)
+// stays cache-resident while the vocabulary tiles stream past it.  Rows are
+// independent, so the chunking changes no bit of any row.
 hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
                        const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
                        float* lse, void* workspace, const WsLayout& L, hipStream_t s) {
@@ -44,11 +47,16 @@ hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, cons
   float* pm = at<float>(workspace, L.pm);
   float* ps = at<float>(workspace, L.ps);
   float* zt = at<float>(workspace, L.ztgt);
-  hipError_t e = launch_rmsnorm_fwd(x, gamma, eps, T, H, hhat, s);
-  if (e == hipSuccess) e = launch_lmhead_fwd(hhat, W, target, T, H, V, pm, ps, zt, nullptr, s);
-  if (e == hipSuccess)
-    e = launch_lse_combine(pm, ps, zt, T, V, logprob, lse, nullptr, nullptr, nullptr, nullptr, 0,
-                           nullptr, s);
+  hipError_t e = hipSuccess;
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, s);
+    if (e == hipSuccess)
+      e = launch_lmhead_fwd(hhat, W, target + c0, tc, H, V, pm, ps, zt, nullptr, s);
+    if (e == hipSuccess)
+      e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse ? lse + c0 : nullptr, nullptr,
+                             nullptr, nullptr, nullptr, 0, nullptr, s);
+  }
   return e;
 }
 

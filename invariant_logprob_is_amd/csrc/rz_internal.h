@@ -32,7 +32,7 @@ inline int64_t shift_stride(int64_t tc) { return round_up(tc, kTile); }
 // Workspace layout; every region starts on a 256-byte boundary.  Regions of
 // different entry points overlap (calls on one workspace are ordered).
 struct WsLayout {
-  // rz_logprob
+  // rz_logprob (chunks of at most kBwdChunk tokens)
   size_t hhat, pm, ps, ztgt, fwd_end;
   // rz_backward (chunks of at most kBwdChunk tokens)
   size_t b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, bwd_end;
@@ -45,16 +45,15 @@ struct WsLayout {
 
 inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   WsLayout L{};
-  const int64_t Tp = round_up(T, kTile);
   const int64_t nvt = n_vocab_tiles(V);
   const int64_t Vp = vocab_pad(V);
   const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
   const int64_t tcp = shift_stride(tc);
   size_t o = 0;
-  L.hhat = o;  o = align256(o + size_t(Tp) * H * 2);
-  L.pm = o;    o = align256(o + size_t(nvt) * T * 4);
-  L.ps = o;    o = align256(o + size_t(nvt) * T * 4);
-  L.ztgt = o;  o = align256(o + size_t(T) * 4);
+  L.hhat = o;  o = align256(o + size_t(tc) * H * 2);
+  L.pm = o;    o = align256(o + size_t(nvt) * tc * 4);
+  L.ps = o;    o = align256(o + size_t(nvt) * tc * 4);
+  L.ztgt = o;  o = align256(o + size_t(tc) * 4);
   L.fwd_end = o;
   o = 0;
   L.b_hhat = o; o = align256(o + size_t(tc) * H * 2);

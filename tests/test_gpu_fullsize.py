@@ -1,6 +1,7 @@
 """Full-size runs in the launch configuration the benchmark times (the whole
 batch in one rz_learner_step call), checked on sampled rows against the
-oracle and on properties that hold at any size.
+oracle and on properties that hold at any size; and the decomposition probe
+at full size.
 
 The rollout log-probability here is a stand-in that neither implementation
 produced: mu = -ln V + lag noise.  (The benchmark follows the workload recipe
@@ -80,3 +81,34 @@ def test_full_size_sampled_rows(gpu, cfg):
     assert e <= 1e-3
     np.testing.assert_allclose(host(adv), oracle.advantages(b.reward, b.group_offsets),
                                rtol=1e-7, atol=1e-7)
+
+
+def test_full_size_decompose_has_zero_mismatch(gpu):
+    """The decomposition probe at the 1.5B shape: mu recorded at the rollout's
+    weights in a different batching (odd-sized chunks) leaves exactly zero
+    kernel mismatch on every token; the lag matches the oracle on sampled
+    rows."""
+    import invariant_logprob_is_amd as rz
+    b = workloads.qwen15b()
+    T, H, V = b.T, b.H, b.V
+    _, g_old, W_old = workloads.older_version(1, b.x[:1], b.gamma, b.W, 1e-3, 0.0, 0.0)
+    say(f"decompose full size T={T}")
+    x, g, W, t = bf16(b.x, gpu), bf16(b.gamma, gpu), bf16(b.W, gpu), i32(b.target, gpu)
+    Wo, go = bf16(W_old, gpu), bf16(g_old, gpu)
+    mu = torch.empty(T, dtype=torch.float32, device=gpu)
+    ws = torch.empty(rz.workspace_bytes(T, H, V), dtype=torch.uint8, device=gpu)
+    for a in range(0, T, 8191):
+        c = min(T, a + 8191)
+        lp, _ = rz.logprob(x[a:c], go, Wo, t[a:c], b.eps, workspace=ws)
+        mu[a:c] = lp
+    out = rz.decompose(x, g, W, x, go, Wo, t, mu, b.eps, workspace=ws)
+    summ = host(out["summary"])
+    say(f"  max|lag|={summ[0]:.3e} mean lag={summ[1]:.3e} tokens with mismatch={int(summ[3])}")
+    assert summ[3] == 0.0 and summ[2] == 0.0
+    rows = _sample_rows(T, 96, seed=7)
+    olp_new, _ = oracle.logprob(b.x[rows], b.gamma, b.eps, b.W, b.target[rows])
+    olp_old, _ = oracle.logprob(b.x[rows], g_old, b.eps, W_old, b.target[rows])
+    olag, _ = oracle.decompose(olp_new, olp_old, host(mu)[rows])
+    err = np.abs(host(out["lag"])[rows] - olag).max()
+    say(f"  sampled rows: max|dlag|={err:.2e}")
+    assert err <= 1e-3
