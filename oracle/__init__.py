@@ -37,7 +37,7 @@ import numpy as np
 __all__ = [
     "bf16_decode", "bf16_round", "rmsnorm", "logits", "log_softmax_gather",
     "logprob", "advantages", "is_weights", "is_loss", "is_coef_rows", "d3", "kl_estimators",
-    "peak_median", "decompose", "logit_grad",
+    "peak_median", "decompose", "logit_grad", "weight_grads",
     "rmsnorm_backward", "backward", "learner_step",
 ]
 
@@ -306,6 +306,35 @@ def backward(x_bits, gamma_bits, eps, W_bits, target, lse, coef, row_chunk: int 
         dh = logit_grad(z, lse[a:b], target[a:b], coef[a:b]) @ Wv
         out[a:b] = rmsnorm_backward(x_bits[a:b], gamma_bits, eps, dh)
     return out
+
+
+def weight_grads(x_bits, gamma_bits, eps, W_bits, target, lse, coef, row_chunk: int = 256,
+                 round_hhat: bool = True):
+    """The gradients of the loss with respect to the LM-head weight and the
+    RMSNorm weight, for given per-token lse and coef (the rest of the
+    learner head's backward; the pages' update step applies the gradient of
+    the loss above to all weights, [P2] "Alignment permits a simpler learning
+    path").  With dlogits = coef (onehot - p) as in logit_grad:
+        dW[v, k] = sum_t dlogits[t, v] hhat[t, k],
+        dgamma[k] = sum_t dhhat[t, k] x[t, k] r_t,   dhhat = dlogits W,
+    the second because y = gamma x r and the bf16 rounding of y is treated as
+    the identity (straight-through), as in rmsnorm_backward.  The logits and
+    dW use the rounded hhat, as the forward does (round_hhat=False drops that
+    rounding, for the finite-difference pins).  Row chunked; float64.
+    Returns (dW [V, H], dgamma [H])."""
+    Wv = _vals(W_bits)
+    x = _vals(x_bits)
+    T = x.shape[0]
+    V, H = Wv.shape
+    dW = np.zeros((V, H))
+    dg = np.zeros(H)
+    for a in range(0, T, row_chunk):
+        b = min(T, a + row_chunk)
+        hh, r = rmsnorm(x_bits[a:b], gamma_bits, eps, round_output=round_hhat)
+        g = logit_grad(logits(hh, Wv), lse[a:b], target[a:b], coef[a:b])
+        dW += g.T @ hh
+        dg += np.sum((g @ Wv) * x[a:b] * r[:, None], axis=0)
+    return dW, dg
 
 
 def learner_step(x_bits, gamma_bits, eps, W_bits, target, mu, resp_offsets, group_offsets, reward):

@@ -366,6 +366,72 @@ def test_backward_matches_torch_autograd():
     np.testing.assert_allclose(dx, xt.grad.numpy(), rtol=1e-10, atol=1e-14)
 
 
+def test_weight_grads_match_finite_differences():
+    rng = np.random.default_rng(12)
+    T, H, V = 7, 12, 23
+    xv = rng.standard_normal((T, H))
+    gv = 1 + 0.1 * rng.standard_normal(H)
+    Wv = 0.3 * rng.standard_normal((V, H))
+    tgt = rng.integers(0, V, T).astype(np.int32)
+    tgt[3] = tgt[1]                     # two tokens share a target row
+    ro = np.array([0, 3, 4, 7]); go = np.array([0, 3])
+    reward = np.array([1.0, 0.0, 0.25], np.float32)
+    mu = -np.log(V) + 0.3 * rng.standard_normal(T)
+    eps = 1e-6
+    hh, _ = oracle.rmsnorm(xv, gv, eps, round_output=False)
+    lp, lse = oracle.log_softmax_gather(oracle.logits(hh, Wv), tgt)
+    coef = oracle.is_loss(lp, mu, ro, go, reward)["coef"]
+    dW, dg = oracle.weight_grads(xv, gv, eps, Wv, tgt, lse, coef, round_hhat=False)
+    h = 1e-6
+    fdW = np.zeros_like(Wv)
+    for v in range(V):
+        for k in range(H):
+            Wp = Wv.copy(); Wp[v, k] += h
+            Wm = Wv.copy(); Wm[v, k] -= h
+            fdW[v, k] = (_chain_loss(xv, gv, eps, Wp, tgt, mu, ro, go, reward)
+                         - _chain_loss(xv, gv, eps, Wm, tgt, mu, ro, go, reward)) / (2 * h)
+    fdg = np.zeros_like(gv)
+    for k in range(H):
+        gp = gv.copy(); gp[k] += h
+        gm = gv.copy(); gm[k] -= h
+        fdg[k] = (_chain_loss(xv, gp, eps, Wv, tgt, mu, ro, go, reward)
+                  - _chain_loss(xv, gm, eps, Wv, tgt, mu, ro, go, reward)) / (2 * h)
+    np.testing.assert_allclose(dW, fdW, rtol=1e-6, atol=1e-9 * np.abs(fdW).max())
+    np.testing.assert_allclose(dg, fdg, rtol=1e-6, atol=1e-9 * np.abs(fdg).max())
+
+
+def test_weight_grads_match_torch_autograd_and_invariants():
+    rng = np.random.default_rng(13)
+    T, H, V = 10, 16, 37
+    xv = rng.standard_normal((T, H))
+    gv = 1 + 0.1 * rng.standard_normal(H)
+    Wv = 0.2 * rng.standard_normal((V, H))
+    tgt = rng.integers(0, V, T)
+    mu = -np.log(V) + 0.2 * rng.standard_normal(T)
+    eps = 1e-6
+    Wt = torch.tensor(Wv, requires_grad=True)
+    gt = torch.tensor(gv, requires_grad=True)
+    y = torch.nn.functional.rms_norm(torch.tensor(xv), (H,), weight=gt, eps=float(np.float32(eps)))
+    logp = torch.log_softmax(y @ Wt.T, dim=1)[torch.arange(T), torch.tensor(tgt)]
+    w = torch.exp(logp - torch.tensor(mu))
+    A = torch.tensor([0.5, -0.5], dtype=torch.float64)
+    loss = -(A[0] * w[0:6].mean() + A[1] * w[6:10].mean()) / 2
+    loss.backward()
+    ro = np.array([0, 6, 10]); go = np.array([0, 2])
+    reward = np.array([1.0, 0.0], np.float32)
+    hh, _ = oracle.rmsnorm(xv, gv, eps, round_output=False)
+    lp, lse = oracle.log_softmax_gather(oracle.logits(hh, Wv), tgt)
+    coef = oracle.is_loss(lp, mu, ro, go, reward)["coef"]
+    dW, dg = oracle.weight_grads(xv, gv, eps, Wv, tgt, lse, coef, round_hhat=False)
+    np.testing.assert_allclose(dW, Wt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    np.testing.assert_allclose(dg, gt.grad.numpy(), rtol=1e-10, atol=1e-15)
+    # every column of dW sums to 0 (each dlogits row sums to 0)
+    assert np.abs(dW.sum(axis=0)).max() <= 1e-14 * np.abs(dW).max() * V
+    # zero coef: zero gradients
+    z = oracle.weight_grads(xv, gv, eps, Wv, tgt, lse, np.zeros(T), round_hhat=False)
+    assert not np.any(z[0]) and not np.any(z[1])
+
+
 def test_backward_invariants():
     x, g, W, tgt = _small_case(13, T=11, H=32, V=40)
     eps = 1e-6
