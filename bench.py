@@ -214,6 +214,9 @@ def main():
                     choices=["qwen15b", "qwen4b_lag64", "a3b30_head", "tiny"])
     ap.add_argument("--cpu-tokens", type=int, default=8192)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--grads", action="store_true",
+                    help="also compute the weight gradients dW, dgamma in the timed step "
+                         "(6*H*V algorithmic flops per token instead of 4*H*V)")
     ap.add_argument("--probe", action="store_true",
                     help="time the log-ratio decomposition probe (rz_decompose) and track the KL "
                          "estimators over synthetic updates instead of the learner step")
@@ -249,7 +252,8 @@ def main():
     go = torch.from_numpy(b.group_offsets).to(dev)
     reward = torch.from_numpy(b.reward).to(dev)
     rz.validate_offsets(b.resp_offsets, b.group_offsets, b.T)
-    ws = torch.empty(rz.workspace_bytes(b.T, b.H, b.V), dtype=torch.uint8, device=dev)
+    ws_need = (rz.workspace_bytes_grads if args.grads else rz.workspace_bytes)(b.T, b.H, b.V)
+    ws = torch.empty(ws_need, dtype=torch.uint8, device=dev)
     lp = torch.empty(b.T, dtype=torch.float32, device=dev)
     lse = torch.empty(b.T, dtype=torch.float32, device=dev)
     dh = torch.empty(b.T, b.H, dtype=torch.float32, device=dev)
@@ -263,6 +267,9 @@ def main():
             "coef": torch.empty(b.T, dtype=torch.float32, device=dev),
             "loss": torch.empty(1, dtype=torch.float64, device=dev),
             "d3": torch.empty(1, dtype=torch.float64, device=dev)}
+    if args.grads:
+        outs["dW"] = torch.empty(b.V, b.H, dtype=torch.float32, device=dev)
+        outs["dgamma"] = torch.empty(b.H, dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream(dev)
     # a plain copy of known size: the reference for the HBM byte counters
@@ -275,7 +282,8 @@ def main():
         return
 
     def step():
-        rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs)
+        rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs,
+                        weight_grads=args.grads)
 
     for i in range(args.warmup):
         step()
@@ -303,10 +311,10 @@ def main():
 
     T, H, V = b.T, b.H, b.V
     tokens_per_s = T / (ms_step / 1000.0)
-    alg_flops_token = 4.0 * H * V
-    gemm_flops_step = 2.0 * T * H * V      # algorithmic flops of each of the two GEMM kernels per step
+    alg_flops_token = (6.0 if args.grads else 4.0) * H * V
+    gemm_flops_step = 2.0 * T * H * V      # algorithmic flops of each GEMM kernel per step
     kernels = {}
-    for k in ("k_lmhead_fwd", "k_dhidden"):
+    for k in ("k_lmhead_fwd", "k_dhidden") + (("k_dw",) if args.grads else ()):
         tot, n = prof.get(k, (float("nan"), 0))
         achieved = gemm_flops_step * args.steps / (tot / 1000.0)
         kernels[k] = {"ms_per_step": tot / args.steps, "launches_per_step": n // args.steps,
@@ -317,8 +325,12 @@ def main():
         "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s", "frac": kernels[dom]["frac"],
         "traffic": measured_traffic(dom),
     }
+    metric = "learner tokens/sec (fwd+bwd logprob+IS loss) and % bf16 MFMA peak, 1 GPU"
+    if args.grads:
+        metric = ("learner tokens/sec (fwd+bwd logprob+IS loss, with LM-head dW and RMSNorm "
+                  "dgamma) and % bf16 MFMA peak, 1 GPU")
     out = {
-        "metric": "learner tokens/sec (fwd+bwd logprob+IS loss) and % bf16 MFMA peak, 1 GPU",
+        "metric": metric,
         "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",

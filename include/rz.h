@@ -73,6 +73,14 @@ const char* rz_status_string(int status);
 size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
 
 /*
+ * rz_workspace_bytes_grads -- workspace for rz_learner_step with the weight
+ * gradients (dW, dgamma): the above plus one chunk of the transposed
+ * probabilities and hidden states (about another 10 GB at V = 151,936).
+ * 0 for invalid sizes.
+ */
+size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
+
+/*
  * rz_logprob -- batch-invariant learner log-probabilities.
  *
  * Computes, for every row t < T:
@@ -232,7 +240,21 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
  * logprob [T] fp32; lse [T] fp32 (may be NULL); loss [1] fp64; d3 [1] fp64;
  * kl [3] fp64 (may be NULL; as rz_kl); coef [T] fp32 (may be NULL);
  * dhidden [T,H] fp32.
- * Errors: the union of those of rz_logprob and rz_is_loss.
+ *
+ * Weight gradients (dW and dgamma both given, or both NULL): the rest of the
+ * head's backward, the gradient of the same loss with respect to the LM-head
+ * weight and the RMSNorm weight ([P2] "Alignment permits a simpler learning
+ * path": the update applies the loss gradient to the weights):
+ *   dW[v] = sum_t coef_t (onehot(target_t)_v - p_tv) hhat_t      [V,H] fp32
+ *   dgamma[k] = sum_t dhhat_tk x_tk r_t                          [H] fp32
+ * (the bf16 rounding of hhat is straight-through).  The softmax part is
+ * contracted on bf16 MFMA from coef_t p_tv rounded once to bf16, fp32
+ * accumulation, chunks added in order; the one-hot part is added exactly in
+ * fp32, per target row in token order; dgamma is summed in float64 in a
+ * fixed order.  Deterministic run to run.  They need the larger workspace
+ * of rz_workspace_bytes_grads.
+ * Errors: the union of those of rz_logprob and rz_is_loss; RZ_EINVAL also for
+ * exactly one of dW, dgamma NULL.
  */
 int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
                     const uint16_t* W, const int32_t* target,
@@ -241,7 +263,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
                     const int64_t* group_offsets, int32_t G,
                     const float* reward,
                     float* logprob, float* lse, double* loss, double* d3, double* kl,
-                    float* coef, float* dhidden,
+                    float* coef, float* dhidden, float* dW, float* dgamma,
                     void* workspace, size_t workspace_bytes, void* stream);
 
 /*

@@ -20,7 +20,7 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RzError", "lib", "version", "workspace_bytes", "logprob", "is_loss", "d3", "kl",
+    "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "logprob", "is_loss", "d3", "kl",
     "decompose", "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH",
     "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
@@ -41,6 +41,7 @@ SYMBOLS = {
     "rz_version": (ctypes.c_int, []),
     "rz_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rz_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
+    "rz_workspace_bytes_grads": (_SZ, [_I64, _I32, _I32]),
     "rz_logprob": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
@@ -49,7 +50,8 @@ SYMBOLS = {
     "rz_decompose": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P,
                                     _P, _P, _SZ, _P]),
     "rz_learner_step": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _P, _I32, _P,
-                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P]),
+                                       _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
+                                       _P]),
     "rz_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "rz_profile_count": (ctypes.c_int, []),
     "rz_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -88,6 +90,11 @@ def version() -> int:
 
 def workspace_bytes(T: int, H: int, V: int) -> int:
     return int(lib().rz_workspace_bytes(T, H, V))
+
+
+def workspace_bytes_grads(T: int, H: int, V: int) -> int:
+    """Workspace of learner_step with weight_grads (rz_workspace_bytes_grads)."""
+    return int(lib().rz_workspace_bytes_grads(T, H, V))
 
 
 def _check(fn: str, status: int):
@@ -312,13 +319,15 @@ def backward(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, workspace=Non
 
 
 def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offsets, reward,
-                 eps: float = 1e-6, *, workspace=None, out=None):
+                 eps: float = 1e-6, *, workspace=None, out=None, weight_grads: bool = False):
     """The whole learner head for one update (rz_learner_step): per-token
     log-probabilities (bit-identical to logprob()), the IS loss, D3, the
     per-token loss gradient coef and dhidden, computing the logits once.
 
     Returns a dict with logprob, lse, coef [T] fp32, loss, d3 [1] fp64,
-    kl [3] fp64 (k1, k2, k3 as kl()) and dhidden [T,H] fp32.  `out` may supply preallocated tensors for any of
+    kl [3] fp64 (k1, k2, k3 as kl()) and dhidden [T,H] fp32; with
+    weight_grads also dW [V,H] and dgamma [H] fp32 (the larger workspace of
+    workspace_bytes_grads).  `out` may supply preallocated tensors for any of
     these keys."""
     torch = _torch()
     dev = x.device
@@ -346,17 +355,23 @@ def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offse
              "coef": ((T,), torch.float32), "loss": ((1,), torch.float64),
              "d3": ((1,), torch.float64), "kl": ((3,), torch.float64),
              "dhidden": ((T, H), torch.float32)}
+    if weight_grads:
+        specs["dW"] = ((V, H), torch.float32)
+        specs["dgamma"] = ((H,), torch.float32)
     for k, (shape, dt) in specs.items():
         if k not in o:
             o[k] = torch.empty(shape, dtype=dt, device=dev)
         _need(o[k], k, dt, dev, len(shape))
-    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    need = workspace_bytes_grads(T, H, V) if weight_grads else workspace_bytes(T, H, V)
+    ws = _workspace(need, dev, workspace)
+    dW = o["dW"].data_ptr() if weight_grads else None
+    dg = o["dgamma"].data_ptr() if weight_grads else None
     st = lib().rz_learner_step(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
                                target.data_ptr(), rollout_logprob.data_ptr(), T, H, V,
                                ro.data_ptr(), R, go.data_ptr(), G, rw.data_ptr(),
                                o["logprob"].data_ptr(), o["lse"].data_ptr(), o["loss"].data_ptr(),
                                o["d3"].data_ptr(), o["kl"].data_ptr(), o["coef"].data_ptr(),
-                               o["dhidden"].data_ptr(),
+                               o["dhidden"].data_ptr(), dW, dg,
                                ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_learner_step", st)
     return o

@@ -83,6 +83,12 @@ size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V) {
   return ws_layout(T, H, V).total;
 }
 
+size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V) {
+  if (T < 1 || H < 1 || V < 1) return 0;
+  const WsLayout L = ws_layout(T, H, V);
+  return L.grads_end > L.total ? L.grads_end : L.total;
+}
+
 int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
                const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
@@ -235,7 +241,8 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
                     int32_t V, const int64_t* resp_offsets, int32_t R,
                     const int64_t* group_offsets, int32_t G, const float* reward, float* logprob,
                     float* lse, double* loss, double* d3, double* kl, float* coef, float* dhidden,
-                    void* workspace, size_t workspace_bytes, void* stream) {
+                    float* dW, float* dgamma, void* workspace, size_t workspace_bytes,
+                    void* stream) {
   if (!x || !gamma || !W || !target || !rollout_logprob || !resp_offsets || !group_offsets ||
       !reward || !logprob || !loss || !d3 || !dhidden || !workspace)
     return RZ_EINVAL;
@@ -246,11 +253,14 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
       (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return RZ_EINVAL;
   if (!(eps >= 0.0f)) return RZ_EINVAL;
+  if ((dW == nullptr) != (dgamma == nullptr)) return RZ_EINVAL;
+  if ((dW && !aligned4(dW)) || (dgamma && !aligned4(dgamma))) return RZ_EINVAL;
   int st = check_head_shape(T, H, V);
   if (st != RZ_OK) return st;
   if (R < 1 || G < 1 || int64_t(R) > T || G > R) return RZ_EINVAL;
   const WsLayout L = ws_layout(T, H, V);
-  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  const bool grads = dW != nullptr;
+  if (workspace_bytes < L.total || (grads && workspace_bytes < L.grads_end)) return RZ_EWORKSPACE;
   st = check_device();
   if (st != RZ_OK) return st;
 
@@ -282,6 +292,12 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     if (e == hipSuccess)
       e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef_ + c0, tc, H, V, dhidden + c0 * H,
                          s);
+    if (e == hipSuccess && grads)
+      e = launch_weight_grads_chunk(E, D, ds, g, coef_ + c0, target + c0, hh, x + c0 * H, eps,
+                                    dhidden + c0 * H, tc, H, V, c0 / kTile, c0 == 0,
+                                    at<uint16_t>(workspace, L.g_pt), at<uint16_t>(workspace, L.g_ht),
+                                    at<int32_t>(workspace, L.g_ibuf),
+                                    at<double>(workspace, L.g_part), dW, s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
   if (e == hipSuccess)
@@ -289,6 +305,8 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
                        loss, nullptr, nullptr, part, s);
   if (e == hipSuccess) e = launch_d3(logprob, rollout_logprob, T, d3, part, s);
   if (e == hipSuccess && kl) e = launch_kl(logprob, rollout_logprob, T, kl, part, s);
+  if (e == hipSuccess && grads)
+    e = launch_dgamma_final(at<double>(workspace, L.g_part), ceil_div(T, kTile), H, dgamma, s);
   return status_of(e);
 }
 

@@ -754,6 +754,291 @@ __global__ __launch_bounds__(256) void k_decompose_final(const double* __restric
 }
 
 // ---------------------------------------------------------------------------
+// Weight gradients (optional outputs of the learner step).
+//   dW[v] = sum_t coef_t (onehot(target_t)_v - p_tv) hhat_t
+//   dgamma[k] = sum_t dhhat[t, k] x[t, k] r_t
+// The softmax part is a contraction over tokens: Pt[v][t] = coef_t p_tv is
+// formed from the stored e (exact exponent shift, then the factor coef_t g_t
+// in fp32, one rounding to bf16), hhat is transposed, and the same 256x256
+// MFMA tile core computes Pt * hhat^T.  Chunks add into dW in chunk order.
+// The one-hot part is added exactly in fp32, per target row in token order,
+// after a deterministic bucketing of the chunk's tokens by target.
+// ---------------------------------------------------------------------------
+
+// Pt[v][t] for a 64 x 64 (vocabulary x token) block: 8 e fragments in, a
+// transpose through LDS, 128-byte row segments out.  Tokens past TC and
+// vocabulary rows past V come out as 0.
+__global__ __launch_bounds__(256) void k_transpose_p(const uint16_t* __restrict__ E,
+                                                     const uint32_t* __restrict__ D, int64_t ds,
+                                                     const float* __restrict__ gf,
+                                                     const float* __restrict__ coef, int64_t TC,
+                                                     int64_t Vp, int64_t TCp,
+                                                     uint16_t* __restrict__ Pt) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t v0 = int64_t(blockIdx.x) * 64;
+  const int64_t t0 = int64_t(blockIdx.y) * 64;
+  const int64_t n_ks = Vp / 16;
+  const int64_t tt = t0 / kTile;
+  const int64_t j = v0 / kTile;                    // vocabulary tile of the whole block
+  const int tid = threadIdx.x;
+  // 8 fragments (4 vocabulary steps x 2 token blocks) x 64 lanes of 16 B:
+  // thread tid takes fragment slot pairs (tid, tid + 256) of the 512.
+#pragma unroll
+  for (int u = 0; u < 2; ++u) {
+    const int q = tid + u * 256;                   // 0..511
+    const int f = q >> 6;                          // fragment 0..7
+    const int lane = q & 63;
+    const int ksl = f >> 1, mbl = f & 1;
+    const int64_t ks = v0 / 16 + ksl;
+    const int64_t mb = (t0 % kTile) / 32 + mbl;
+    const int tl = mbl * 32 + (lane & 31);        // token within the block
+    const int vl = ksl * 16 + 8 * (lane >> 5);     // first vocabulary row within the block
+    const int64_t t = t0 + tl;
+    float sc = 0.0f;
+    uint32_t d = 255u;
+    if (t < TC && ks < n_ks) {
+      sc = coef[t] * gf[t];
+      d = (D[j * ds + t] & 0xFFFFu) >> 7;
+    }
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (ks < n_ks)
+      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(E) +
+                                          frag_offset(tt, ks, mb, n_ks) + lane * 16);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const float e = __uint_as_float(h ? (w[c] & 0xFFFF0000u) : (w[c] << 16));
+        const float p = (d >= 255u) ? 0.0f : ldexpf(e, -int(d)) * sc;
+        tile[vl + 2 * c + h][tl] = f32_to_bf16_rne(p);
+      }
+    }
+  }
+  __syncthreads();
+  const int row = tid >> 2;                        // vocabulary row within the block
+  const int seg = tid & 3;                         // 16-token segment
+  const int64_t v = v0 + row;
+  if (v < Vp) {
+    u32x4 a, b;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      a[c] = uint32_t(tile[row][seg * 16 + 2 * c]) | (uint32_t(tile[row][seg * 16 + 2 * c + 1]) << 16);
+      b[c] = uint32_t(tile[row][seg * 16 + 8 + 2 * c]) |
+             (uint32_t(tile[row][seg * 16 + 8 + 2 * c + 1]) << 16);
+    }
+    uint16_t* dst = Pt + v * TCp + t0 + seg * 16;
+    *reinterpret_cast<u32x4*>(dst) = a;
+    *reinterpret_cast<u32x4*>(dst + 8) = b;
+  }
+}
+
+// The softmax part of dW for a chunk: dW[v][h] = (first ? 0 : dW[v][h]) -
+// sum_t Pt[v][t] hT[h][t].  Operand A = Pt (vocabulary rows, K = TCp
+// tokens), operand B = hT (hidden rows).
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_dw(const uint16_t* __restrict__ Pt, const uint16_t* __restrict__ hT, int64_t TCp, int H,
+          int V, int64_t n_vt, int64_t n_ht, int first, float* __restrict__ dW) {
+  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  int64_t vt, ht;
+  if (!tile_of(n_vt, n_ht, vt, ht)) return;
+  const int64_t v0 = vt * kTile;
+  const int64_t h0 = ht * kTile;
+  GemmCore g;
+  g.init(Pt, v0, V, hT, h0, H, TCp, lds);
+  g.run(int(TCp));
+  f32x16 (&acc)[4][4] = g.acc;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int64_t v = v0 + acc_row(wm, i, r, lane);
+      if (v >= V) continue;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int64_t h = h0 + acc_col(wn, j, lane);
+        if (h < H) {
+          float* o = dW + v * H + h;
+          *o = (first ? 0.0f : *o) - acc[i][j][r];
+        }
+      }
+    }
+  }
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// Tokens of a chunk per target row: count, then (k_scan_*) the bucket
+// offsets, then the tokens in each bucket (any order), then their order by
+// token index (rank = tokens of the bucket with a smaller index).
+__global__ __launch_bounds__(256) void k_bucket_count(const int32_t* __restrict__ target,
+                                                      int64_t TC, int V, int32_t* count) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= TC) return;
+  const int32_t v = target[t];
+  if (v >= 0 && v < V) atomicAdd(count + v, 1);
+}
+
+// Exclusive prefix sum of count[0..V) into off[0..V] (off[V] = total) in
+// three fixed-order phases over 1024-entry blocks: block totals, a scan of
+// the totals (one workgroup), then each block's scan from its base.
+__device__ __forceinline__ int32_t block_incl_scan_1024(int32_t v, int32_t* sh) {
+  const int tid = threadIdx.x;
+  sh[tid] = v;
+  __syncthreads();
+  for (int w = 1; w < 1024; w <<= 1) {
+    const int32_t add = tid >= w ? sh[tid - w] : 0;
+    __syncthreads();
+    sh[tid] += add;
+    __syncthreads();
+  }
+  return sh[tid];
+}
+
+__global__ __launch_bounds__(1024) void k_scan_blocks(const int32_t* __restrict__ count, int V,
+                                                      int32_t* __restrict__ btot) {
+  __shared__ int32_t sh[1024];
+  const int64_t i = int64_t(blockIdx.x) * 1024 + threadIdx.x;
+  const int32_t v = i < V ? count[i] : 0;
+  const int32_t inc = block_incl_scan_1024(v, sh);
+  if (threadIdx.x == 1023) btot[blockIdx.x] = inc;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_totals(int32_t* __restrict__ btot, int nb) {
+  __shared__ int32_t sh[1024];
+  // nb <= 1024 * 1024 / 1024: one pass of up to 1024 totals per thread group
+  int32_t carry = 0;
+  for (int base = 0; base < nb; base += 1024) {
+    const int i = base + threadIdx.x;
+    const int32_t v = i < nb ? btot[i] : 0;
+    const int32_t inc = block_incl_scan_1024(v, sh);
+    __syncthreads();
+    if (i < nb) btot[i] = carry + inc - v;        // exclusive base of block i
+    carry += sh[1023];
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) btot[nb] = carry;
+}
+
+__global__ __launch_bounds__(1024) void k_scan_apply(const int32_t* __restrict__ count, int V,
+                                                     const int32_t* __restrict__ btot, int nb,
+                                                     int32_t* __restrict__ off) {
+  __shared__ int32_t sh[1024];
+  const int64_t i = int64_t(blockIdx.x) * 1024 + threadIdx.x;
+  const int32_t v = i < V ? count[i] : 0;
+  const int32_t inc = block_incl_scan_1024(v, sh);
+  if (i < V) off[i] = btot[blockIdx.x] + inc - v;
+  if (blockIdx.x == 0 && threadIdx.x == 0) off[V] = btot[nb];
+}
+
+__global__ __launch_bounds__(256) void k_bucket_fill(const int32_t* __restrict__ target,
+                                                     int64_t TC, int V,
+                                                     const int32_t* __restrict__ off,
+                                                     int32_t* cursor, int32_t* __restrict__ slot) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= TC) return;
+  const int32_t v = target[t];
+  if (v >= 0 && v < V) slot[off[v] + atomicAdd(cursor + v, 1)] = int32_t(t);
+}
+
+__global__ __launch_bounds__(256) void k_bucket_order(const int32_t* __restrict__ target,
+                                                      int64_t TC, int V,
+                                                      const int32_t* __restrict__ off,
+                                                      const int32_t* __restrict__ count,
+                                                      const int32_t* __restrict__ slot,
+                                                      int32_t* __restrict__ sorted) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= TC) return;
+  const int32_t v = target[t];
+  if (v < 0 || v >= V) return;
+  const int32_t a = off[v], n = count[v];
+  int32_t rank = 0;
+  for (int32_t i = 0; i < n; ++i) rank += (slot[a + i] < int32_t(t)) ? 1 : 0;
+  sorted[a + rank] = int32_t(t);
+}
+
+// dW[v] += sum over the bucket of v, in token order, of coef_t hhat_t
+// (fp32).  One workgroup per bucket start: position i of the sorted order
+// starts a bucket when it is the first token of its target row.
+__global__ __launch_bounds__(256) void k_onehot_add(const int32_t* __restrict__ target,
+                                                    const int32_t* __restrict__ off,
+                                                    const int32_t* __restrict__ count, int V,
+                                                    const int32_t* __restrict__ sorted,
+                                                    const float* __restrict__ coef,
+                                                    const uint16_t* __restrict__ hh, int H,
+                                                    float* __restrict__ dW) {
+  const int32_t i = blockIdx.x;
+  if (i >= off[V]) return;                         // only tokens with a target in [0, V)
+  const int32_t t0 = sorted[i];
+  const int32_t v = target[t0];
+  if (off[v] != i) return;
+  const int32_t n = count[v];
+  for (int h = threadIdx.x; h < H; h += 256) {
+    float acc = 0.0f;
+    for (int32_t q = 0; q < n; ++q) {
+      const int32_t t = sorted[i + q];
+      acc = fmaf(coef[t], bf16_to_f32(hh[int64_t(t) * H + h]), acc);
+    }
+    dW[int64_t(v) * H + h] += acc;
+  }
+}
+
+// r_t = (mean x_t^2 + eps)^(-1/2) of a chunk's rows (float64, as the norm).
+__global__ __launch_bounds__(256) void k_row_rstd(const uint16_t* __restrict__ x, float eps,
+                                                  int64_t TC, int H, double* __restrict__ r) {
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= TC) return;
+  const double ss = row_sumsq(x + t * H, H, threadIdx.x & 63);
+  if ((threadIdx.x & 63) == 0) r[t] = 1.0 / sqrt(ss / double(H) + double(eps));
+}
+
+// dgamma partials: block (b, c) sums dhhat[t, k] x[t, k] r_t over the 256
+// rows of block b in row order (float64) for the 256 columns of block c;
+// global row block gb0 + b.  Loads run 8 rows ahead of the sum.
+__global__ __launch_bounds__(256) void k_dgamma_part(const float* __restrict__ dhh,
+                                                     const uint16_t* __restrict__ x,
+                                                     const double* __restrict__ r, int64_t TC,
+                                                     int H, int64_t gb0,
+                                                     double* __restrict__ part) {
+  const int k = blockIdx.y * 256 + threadIdx.x;
+  if (k >= H) return;
+  const int64_t a = int64_t(blockIdx.x) * 256;
+  const int64_t b = a + 256 < TC ? a + 256 : TC;
+  double s = 0.0;
+  int64_t t = a;
+  for (; t + 8 <= b; t += 8) {
+    float dv[8], xv[8];
+    double rv[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      dv[u] = dhh[(t + u) * H + k];
+      xv[u] = bf16_to_f32(x[(t + u) * H + k]);
+      rv[u] = r[t + u];
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) s += double(dv[u]) * double(xv[u]) * rv[u];
+  }
+  for (; t < b; ++t) s += double(dhh[t * H + k]) * double(bf16_to_f32(x[t * H + k])) * r[t];
+  part[(gb0 + blockIdx.x) * H + k] = s;
+}
+
+__global__ __launch_bounds__(256) void k_dgamma_final(const double* __restrict__ part,
+                                                      int64_t nb, int H,
+                                                      float* __restrict__ dgamma) {
+  const int k = blockIdx.x * 256 + threadIdx.x;
+  if (k >= H) return;
+  double s = 0.0;
+  for (int64_t b = 0; b < nb; ++b) s += part[b * H + k];
+  dgamma[k] = float(s);
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 static inline uint32_t blocks_for(int64_t n, int64_t per) { return uint32_t(ceil_div(n, per)); }
@@ -852,6 +1137,73 @@ hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d
   const int64_t nb = ceil_div(T, kD3Block);
   hipLaunchKernelGGL(k_kl_part, dim3(uint32_t(nb)), dim3(256), 0, s, logprob, mu, T, part);
   hipLaunchKernelGGL(k_kl_final, dim3(1), dim3(256), 0, s, part, nb, T, 1, d3);
+  return hipGetLastError();
+}
+
+hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64_t ds,
+                                    const float* g, const float* coef_chunk,
+                                    const int32_t* target_chunk, const uint16_t* hh,
+                                    const uint16_t* x_chunk, float eps, const float* dhh_chunk,
+                                    int64_t TC, int H, int V, int64_t gb0, int first,
+                                    uint16_t* Pt, uint16_t* hT, int32_t* ibuf, double* gpart,
+                                    float* dW, hipStream_t s) {
+  const int64_t Vp = vocab_pad(V);
+  const int64_t TCp = shift_stride(TC);
+  int32_t* count = ibuf;
+  int32_t* cursor = count + V;
+  int32_t* off = cursor + V;
+  int32_t* slot = off + V + 1;
+  int32_t* sorted = slot + TC;
+  int32_t* btot = sorted + TC;
+  double* rbuf = reinterpret_cast<double*>(
+      reinterpret_cast<char*>(ibuf) + align256(size_t(3 * int64_t(V) + 1 + 2 * TC +
+                                                      ceil_div(V, 1024) + 1) * 4));
+  {
+    ProfScope prof("k_dgamma_part", s);
+    hipLaunchKernelGGL(k_row_rstd, dim3(blocks_for(TC, 4)), dim3(256), 0, s, x_chunk, eps, TC, H,
+                       rbuf);
+    hipLaunchKernelGGL(k_dgamma_part, dim3(blocks_for(TC, 256), blocks_for(H, 256)), dim3(256), 0,
+                       s, dhh_chunk, x_chunk, rbuf, TC, H, gb0, gpart);
+  }
+  {
+    ProfScope prof("k_transpose_p", s);
+    hipLaunchKernelGGL(k_transpose_w, dim3(blocks_for(TCp, 64), H / 64), dim3(256), 0, s, hh, H,
+                       int(TC), TCp, hT);
+    hipLaunchKernelGGL(k_transpose_p, dim3(blocks_for(Vp, 64), uint32_t(TCp / 64)), dim3(256), 0,
+                       s, E, D, ds, g, coef_chunk, TC, Vp, TCp, Pt);
+  }
+  {
+    ProfScope prof("k_dw", s);
+    const int64_t n_vt = n_vocab_tiles(V);
+    const int64_t n_ht = ceil_div(H, kTile);
+    hipLaunchKernelGGL(k_dw, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, Pt, hT, TCp, H,
+                       V, n_vt, n_ht, first, dW);
+  }
+  {
+    ProfScope prof("k_onehot", s);
+    const int nbv = int(ceil_div(V, 1024));
+    hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(2 * int64_t(V), 256)), dim3(256), 0, s, count,
+                       2 * int64_t(V), 0);
+    hipLaunchKernelGGL(k_bucket_count, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
+                       TC, V, count);
+    hipLaunchKernelGGL(k_scan_blocks, dim3(nbv), dim3(1024), 0, s, count, V, btot);
+    hipLaunchKernelGGL(k_scan_totals, dim3(1), dim3(1024), 0, s, btot, nbv);
+    hipLaunchKernelGGL(k_scan_apply, dim3(nbv), dim3(1024), 0, s, count, V, btot, nbv, off);
+    hipLaunchKernelGGL(k_bucket_fill, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
+                       TC, V, off, cursor, slot);
+    hipLaunchKernelGGL(k_bucket_order, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
+                       TC, V, off, count, slot, sorted);
+    hipLaunchKernelGGL(k_onehot_add, dim3(uint32_t(TC)), dim3(256), 0, s, target_chunk, off,
+                       count, V, sorted, coef_chunk, hh, H, dW);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_dgamma_final(const double* gpart, int64_t nb, int H, float* dgamma,
+                               hipStream_t s) {
+  ProfScope prof("k_dgamma_part", s);
+  hipLaunchKernelGGL(k_dgamma_final, dim3(blocks_for(H, 256)), dim3(256), 0, s, gpart, nb, H,
+                     dgamma);
   return hipGetLastError();
 }
 

@@ -173,12 +173,13 @@ def test_decompose_argument_validation():
 def _step(**kw):
     a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, mu=FAKE, T=300, H=128, V=1024,
              ro=FAKE, R=16, go=FAKE, G=4, reward=FAKE, lp=FAKE, lse=FAKE, loss=FAKE, d3=FAKE,
-             kl=FAKE, coef=FAKE, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+             kl=FAKE, coef=FAKE, dh=FAKE, dW=None, dg=None, ws=FAKE, wsb=1 << 40, stream=None)
     a.update(kw)
     return rz.lib().rz_learner_step(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["mu"],
                                     a["T"], a["H"], a["V"], a["ro"], a["R"], a["go"], a["G"],
                                     a["reward"], a["lp"], a["lse"], a["loss"], a["d3"], a["kl"],
-                                    a["coef"], a["dh"], a["ws"], a["wsb"], a["stream"])
+                                    a["coef"], a["dh"], a["dW"], a["dg"], a["ws"], a["wsb"],
+                                    a["stream"])
 
 
 def test_learner_step_argument_validation():
@@ -187,6 +188,13 @@ def test_learner_step_argument_validation():
     assert _step(x=FAKE + 8) == rz.RZ_EINVAL
     assert _step(dh=FAKE + 4) == rz.RZ_EINVAL
     assert _step(kl=FAKE + 4) == rz.RZ_EINVAL      # fp64 output needs 8-byte alignment
+    assert _step(dW=FAKE) == rz.RZ_EINVAL          # dW and dgamma come together
+    assert _step(dg=FAKE) == rz.RZ_EINVAL
+    assert _step(dW=FAKE, dg=FAKE + 2) == rz.RZ_EINVAL
+    # the weight gradients need the larger workspace
+    assert rz.workspace_bytes_grads(300, 128, 1024) > rz.workspace_bytes(300, 128, 1024)
+    assert _step(dW=FAKE, dg=FAKE, wsb=rz.workspace_bytes(300, 128, 1024)) == rz.RZ_EWORKSPACE
+    assert rz.workspace_bytes_grads(0, 128, 1024) == 0
     assert _step(ro=FAKE + 4) == rz.RZ_EINVAL
     assert _step(T=0) == rz.RZ_EINVAL
     assert _step(R=0) == rz.RZ_EINVAL

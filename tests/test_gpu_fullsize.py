@@ -112,3 +112,28 @@ def test_full_size_decompose_has_zero_mismatch(gpu):
     err = np.abs(host(out["lag"])[rows] - olag).max()
     say(f"  sampled rows: max|dlag|={err:.2e}")
     assert err <= 1e-3
+
+
+def test_full_size_weight_grads_properties(gpu):
+    """The weight gradients at the 1.5B shape in the benchmark's launch
+    configuration: finite, every column of dW sums to (nearly) 0 since each
+    row of dlogits does, dgamma finite, and the other outputs unchanged."""
+    import invariant_logprob_is_amd as rz
+    b = workloads.qwen15b()
+    T, H, V = b.T, b.H, b.V
+    say(f"weight grads full size T={T}")
+    mu_np = (np.float32(-math.log(V)) + b.lag_noise).astype(np.float32)
+    x, g, W, t = bf16(b.x, gpu), bf16(b.gamma, gpu), bf16(b.W, gpu), i32(b.target, gpu)
+    mu = f32(mu_np, gpu)
+    ws = torch.empty(rz.workspace_bytes_grads(T, H, V), dtype=torch.uint8, device=gpu)
+    out = rz.learner_step(x, g, W, t, mu, b.resp_offsets, b.group_offsets, b.reward, b.eps,
+                          workspace=ws, weight_grads=True)
+    dW, dg = out["dW"], out["dgamma"]
+    assert torch.isfinite(dW).all().item() and torch.isfinite(dg).all().item()
+    col = dW.double().sum(dim=0).abs()
+    mag = dW.double().abs().sum(dim=0)
+    ratio = (col / mag).max().item()
+    say(f"  max |column sum| / column abs sum = {ratio:.2e}; |dgamma| = {dg.norm().item():.3e}")
+    assert ratio <= 1e-3
+    lp2, _ = rz.logprob(x, g, W, t, b.eps, workspace=ws)
+    assert torch.equal(out["logprob"].view(torch.int32), lp2.view(torch.int32))
