@@ -1,0 +1,70 @@
+"""The largest shapes the ABI accepts, on the GPU, against the oracle on the
+rows and columns it can afford: H = 16384 (the largest hidden size) and
+V = 4,000,000 (the largest vocabulary, whose padded 256-row tiles still keep
+every buffer offset below 2^31 bytes).  Tolerances as in test_gpu_parity."""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import bf16, f32, host, i32, rel_fro, say
+
+pytestmark = pytest.mark.gpu
+
+LP_TOL = 5e-4
+DH_RTOL = 1e-3
+
+
+@pytest.fixture(scope="module")
+def rz():
+    import invariant_logprob_is_amd as m
+    m.lib()
+    return m
+
+
+def _case(seed, T, H, V, wstd):
+    rng = np.random.default_rng(seed)
+    x = workloads.f32_to_bf16_bits(rng.standard_normal((T, H)).astype(np.float32))
+    g = workloads.f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    W = np.empty((V, H), np.uint16)
+    for a in range(0, V, 262144):                 # bounded host memory
+        b = min(V, a + 262144)
+        W[a:b] = workloads.f32_to_bf16_bits((wstd * rng.standard_normal((b - a, H)))
+                                            .astype(np.float32))
+    t = rng.integers(0, V, T).astype(np.int32)
+    return x, g, W, t
+
+
+def test_largest_hidden_size(rz, gpu):
+    T, H, V = 300, 16384, 1024
+    say(f"limits H={H}")
+    x, g, W, t = _case(1, T, H, V, 0.01)
+    d = [bf16(a, gpu) for a in (x, g, W)]
+    lp, lse = rz.logprob(d[0], d[1], d[2], i32(t, gpu))
+    olp, olse = oracle.logprob(x, g, 1e-6, W, t)
+    assert np.abs(host(lp) - olp).max() <= LP_TOL
+    coef = np.random.default_rng(2).normal(0, 1e-2, T).astype(np.float32)
+    dh = rz.backward(d[0], d[1], d[2], i32(t, gpu), lse, f32(coef, gpu))
+    e = rel_fro(host(dh), oracle.backward(x, g, 1e-6, W, t, olse, coef.astype(np.float64)))
+    say(f"  max|dlogprob|={np.abs(host(lp) - olp).max():.2e} dhidden rel_fro={e:.2e}")
+    assert e <= DH_RTOL
+
+
+def test_largest_vocabulary(rz, gpu):
+    T, H, V = 16, 64, 4_000_000
+    say(f"limits V={V}")
+    x, g, W, t = _case(3, T, H, V, 0.05)
+    t[:4] = [0, V - 1, V - 256, V // 2]           # targets in the first, last and a ragged tile
+    d = [bf16(a, gpu) for a in (x, g, W)]
+    lp, lse = rz.logprob(d[0], d[1], d[2], i32(t, gpu))
+    olp, olse = oracle.logprob(x, g, 1e-6, W, t, row_chunk=8)
+    assert np.abs(host(lp) - olp).max() <= LP_TOL
+    assert np.abs(host(lse) - olse).max() <= LP_TOL
+    coef = np.random.default_rng(4).normal(0, 1e-2, T).astype(np.float32)
+    dh = rz.backward(d[0], d[1], d[2], i32(t, gpu), lse, f32(coef, gpu))
+    e = rel_fro(host(dh), oracle.backward(x, g, 1e-6, W, t, olse, coef.astype(np.float64),
+                                          row_chunk=8))
+    say(f"  max|dlogprob|={np.abs(host(lp) - olp).max():.2e} dhidden rel_fro={e:.2e}")
+    assert e <= DH_RTOL
