@@ -50,6 +50,13 @@
 #include <stddef.h>
 #include <stdint.h>
 
+/* Only the entry points below are exported from the shared library. */
+#if defined(__GNUC__) || defined(__clang__)
+#define RZ_API __attribute__((visibility("default")))
+#else
+#define RZ_API
+#endif
+
 #ifdef __cplusplus
 extern "C" {
 #endif
@@ -63,14 +70,14 @@ extern "C" {
 #define RZ_EWORKSPACE 5    /* workspace smaller than rz_workspace_bytes()      */
 
 /* Library version, (major << 16) | (minor << 8) | patch. */
-int rz_version(void);
+RZ_API int rz_version(void);
 
 /* Static, human-readable text for a status code. */
-const char* rz_status_string(int status);
+RZ_API const char* rz_status_string(int status);
 
 /* Workspace size (bytes) that suffices for every entry point below at these
  * sizes.  Returns 0 if the sizes are invalid.  Host only, no HIP call. */
-size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
+RZ_API size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
 
 /*
  * rz_workspace_bytes_grads -- workspace for rz_learner_step with the weight
@@ -78,7 +85,7 @@ size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
  * probabilities and hidden states (about another 10 GB at V = 151,936).
  * 0 for invalid sizes.
  */
-size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
+RZ_API size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
 
 /*
  * rz_logprob -- batch-invariant learner log-probabilities.
@@ -104,7 +111,7 @@ size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
  * RZ_EUNSUPPORTED (H not a multiple of 64, H > 16384, V > 4000000),
  * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
-int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
+RZ_API int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
                const uint16_t* W, const int32_t* target,
                int64_t T, int32_t H, int32_t V,
                float* logprob, float* lse,
@@ -134,7 +141,7 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
  * Errors: RZ_EINVAL (null pointer, T < 1, R < 1, G < 1, R > T, G > R),
  * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
-int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
+RZ_API int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
                const int64_t* resp_offsets, int32_t R,
                const int64_t* group_offsets, int32_t G,
                const float* reward,
@@ -149,7 +156,7 @@ int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
  * Output d3 [1] fp64.
  * Errors: RZ_EINVAL (null pointer, T < 1), RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
-int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
+RZ_API int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
           double* d3, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -165,7 +172,7 @@ int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T,
  * tokens were drawn from mu.  Output kl [3] fp64 (device).
  * Errors: RZ_EINVAL (null pointer, T < 1), RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
-int rz_kl(const float* logprob, const float* rollout_logprob, int64_t T,
+RZ_API int rz_kl(const float* logprob, const float* rollout_logprob, int64_t T,
           double* kl, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
@@ -187,7 +194,7 @@ int rz_kl(const float* logprob, const float* rollout_logprob, int64_t T,
  * (distinct, and distinct from rollout_logprob); workspace as rz_logprob.
  * Errors: as rz_logprob.
  */
-int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_t* W_new,
+RZ_API int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_t* W_new,
                  const uint16_t* x_old, const uint16_t* gamma_old, const uint16_t* W_old,
                  float eps, const int32_t* target, const float* rollout_logprob,
                  int64_t T, int32_t H, int32_t V,
@@ -215,7 +222,7 @@ int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_
  * hands out, dhidden is bit-identical to that call's.
  * Errors: as rz_logprob.
  */
-int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
+RZ_API int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
                 const uint16_t* W, const int32_t* target,
                 const float* lse, const float* coef,
                 int64_t T, int32_t H, int32_t V,
@@ -256,7 +263,7 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
  * Errors: the union of those of rz_logprob and rz_is_loss; RZ_EINVAL also for
  * exactly one of dW, dgamma NULL.
  */
-int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
+RZ_API int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
                     const uint16_t* W, const int32_t* target,
                     const float* rollout_logprob, int64_t T, int32_t H, int32_t V,
                     const int64_t* resp_offsets, int32_t R,
@@ -279,9 +286,9 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps,
  * its launch count.  Recording creates host-side event objects; it takes a
  * process-wide lock, so concurrent callers serialise while it is on.
  */
-int rz_profile_enable(int on);
-int rz_profile_count(void);
-int rz_profile_get(int i, const char** name, double* total_ms, int64_t* launches);
+RZ_API int rz_profile_enable(int on);
+RZ_API int rz_profile_count(void);
+RZ_API int rz_profile_get(int i, const char** name, double* total_ms, int64_t* launches);
 
 #ifdef __cplusplus
 }  /* extern "C" */

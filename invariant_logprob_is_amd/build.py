@@ -23,6 +23,8 @@ LIB = os.path.join(PKG, "librz.so")
 ARCH = "gfx950"
 CFLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
+    # only the C ABI of include/rz.h is exported
+    "-fvisibility=hidden",
     # keep the compiler from forming packed fp32 math on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-function",

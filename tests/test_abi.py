@@ -47,6 +47,20 @@ def test_exports_are_visible_with_dlsym():
         assert ctypes.cast(getattr(raw, n), ctypes.c_void_p).value
 
 
+def test_internal_host_functions_are_not_exported():
+    # the library is built with hidden visibility: the C entry points of
+    # include/rz.h are exported, the C++ launchers and helpers behind them
+    # are not (HIP keeps its kernel stubs visible, which is harmless)
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", rz.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = [line.split()[-1] for line in out.splitlines() if line.strip()]
+    c_names = [n for n in names if n.startswith("rz_")]
+    assert set(c_names) == set(_declared())
+    for n in names:
+        assert "launch_" not in n and "profile_record" not in n and "ws_layout" not in n, n
+
+
 def test_version_and_status_strings():
     assert rz.version() == (0 << 16) | (1 << 8)
     L = rz.lib()
