@@ -183,72 +183,30 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 constexpr int kFwdLds = kLdsBytes + 2048;  // the GEMM ring + the exchange area
 
-template <bool Store>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
-                  const int32_t* __restrict__ target, int64_t T, int H, int V,
-                  int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
-                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
-  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
-  int64_t tt, vt;
-  // Vocabulary tiles are grouped and the token tiles stream past them: the
-  // chunk's hhat (100 MB at H = 1536) stays cache-resident across the
-  // groups, where re-streaming W (467 MB) from HBM for every token group
-  // would not.
-  if (!tile_of(n_vt, n_tt, vt, tt)) return;
+// Steps 1-2 of the epilogue and the partials, on the tile's accumulators.
+// Mask: the last vocabulary tile, whose rows v >= V (read as zeros) count as
+// -inf.  The masked values are formed on the fly instead of written into
+// the accumulators: in-place writes there make the compiler spill in every
+// tile's epilogue.
+template <bool Store, bool Mask>
+__device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* lds, int64_t tt,
+                                             int64_t vt, int64_t T, int V, int64_t Vp,
+                                             float* __restrict__ pm, float* __restrict__ ps,
+                                             uint16_t* __restrict__ E) {
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  GemmCore g;
-  g.init(W, v0, V, hhat, t0, T, H, lds);
-  g.run(H);
-  f32x16 (&acc)[4][4] = g.acc;
-
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int half = lane >> 5;
   const int col = lane & 31;
-  const int64_t vbase = v0 + wm * 128;
-  float* xch = reinterpret_cast<float*>(lds + kFwdLds - 2048);  // [2 waves-rows][4 j][32] x 2
-
-  // Target gather: exactly one lane of one workgroup holds z[t, target[t]].
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t t = t0 + acc_col(wn, j, lane);
-    if (t < T) {
-      const int64_t tg = target[t];
-      const int64_t loc = tg - vbase;
-      if (tg >= 0 && tg < V && loc >= 0 && loc < 128) {
-        const int q = int(loc & 31);
-        if (((q >> 2) & 1) == half) {
-          const int ib = int(loc >> 5);
-          const int rb = ((q >> 3) << 2) | (q & 3);
-          float val = 0.0f;
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-              if (i == ib && r == rb) val = acc[i][j][r];
-          ztgt[t] = val;
-        }
-      }
-    }
-  }
-
-  // Rows past V (last vocabulary tile only) do not exist (they were read as zeros).
-  if (v0 + kTile > V) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int64_t v = v0 + acc_row(wm, i, r, lane);
-        if (v >= V) {
-#pragma unroll
-          for (int j = 0; j < 4; ++j) acc[i][j][r] = -INFINITY;
-        }
-      }
-  }
+  float* xch = reinterpret_cast<float*>(lds + kFwdLds - 2048);
+  // rows of this lane below V: acc_row(wm, i, r, lane) < vlim
+  const int64_t vlim = int64_t(V) - v0;
+  auto val = [&](int i, int j, int r) -> float {
+    return (!Mask || acc_row(wm, i, r, lane) < vlim) ? acc[i][j][r] : -INFINITY;
+  };
 
   // 1. tile max
   float Mj[4];
@@ -258,7 +216,7 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) m = fmaxf(m, acc[i][j][r]);
+      for (int r = 0; r < 16; ++r) m = fmaxf(m, val(i, j, r));
     Mj[j] = fmaxf(m, __shfl_xor(m, 32, 64));
   }
   if (half == 0) {
@@ -290,7 +248,7 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
         float e[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          e[q] = finite ? __builtin_amdgcn_exp2f(fmaf(acc[i][j][r4 * 4 + q], kLog2e, -mb)) : 0.0f;
+          e[q] = finite ? __builtin_amdgcn_exp2f(fmaf(val(i, j, r4 * 4 + q), kLog2e, -mb)) : 0.0f;
           s += e[q];
         }
         if (Store) {
@@ -335,6 +293,63 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
       }
     }
   }
+}
+
+template <bool Store>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
+                  const int32_t* __restrict__ target, int64_t T, int H, int V,
+                  int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
+                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
+  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
+  int64_t tt, vt;
+  // Vocabulary tiles are grouped and the token tiles stream past them: the
+  // chunk's hhat (100 MB at H = 1536) stays cache-resident across the
+  // groups, where re-streaming W (467 MB) from HBM for every token group
+  // would not.
+  if (!tile_of(n_vt, n_tt, vt, tt)) return;
+  const int64_t v0 = vt * kTile;
+  const int64_t t0 = tt * kTile;
+  GemmCore g;
+  g.init(W, v0, V, hhat, t0, T, H, lds);
+  g.run(H);
+  f32x16 (&acc)[4][4] = g.acc;
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave & 1;
+  const int wn = wave >> 1;
+  const int half = lane >> 5;
+  const int64_t vbase = v0 + wm * 128;
+
+  // Target gather: exactly one lane of one workgroup holds z[t, target[t]].
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int64_t t = t0 + acc_col(wn, j, lane);
+    if (t < T) {
+      const int64_t tg = target[t];
+      const int64_t loc = tg - vbase;
+      if (tg >= 0 && tg < V && loc >= 0 && loc < 128) {
+        const int q = int(loc & 31);
+        if (((q >> 2) & 1) == half) {
+          const int ib = int(loc >> 5);
+          const int rb = ((q >> 3) << 2) | (q & 3);
+          float val = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              if (i == ib && r == rb) val = acc[i][j][r];
+          ztgt[t] = val;
+        }
+      }
+    }
+  }
+
+  if (v0 + kTile > V)
+    fwd_tile_lse<Store, true>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
+  else
+    fwd_tile_lse<Store, false>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
 }
 
 // Shift table and row factor that turn the stored e of a token back into its
