@@ -81,8 +81,9 @@ RZ_API size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
 
 /*
  * rz_workspace_bytes_grads -- workspace for rz_learner_step with the weight
- * gradients (dW, dgamma): the above plus one chunk of the transposed
- * probabilities and hidden states (about another 10 GB at V = 151,936).
+ * gradients (dW, dgamma): the above plus one chunk of scaled hidden states
+ * (32768 x H bf16), the per-chunk target buckets and the dgamma partials
+ * (about 120 MB more at H = 1536, V = 151,936 and T = 584,025).
  * 0 for invalid sizes.
  */
 RZ_API size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);

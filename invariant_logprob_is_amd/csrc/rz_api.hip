@@ -295,8 +295,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     if (e == hipSuccess && grads)
       e = launch_weight_grads_chunk(E, D, ds, g, coef_ + c0, target + c0, hh, x + c0 * H, eps,
                                     dhidden + c0 * H, tc, H, V, c0 / kTile, c0 == 0,
-                                    at<uint16_t>(workspace, L.g_pt), at<uint16_t>(workspace, L.g_ht),
-                                    at<int32_t>(workspace, L.g_ibuf),
+                                    at<uint16_t>(workspace, L.g_hs), at<int32_t>(workspace, L.g_ibuf),
                                     at<double>(workspace, L.g_part), dW, s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }

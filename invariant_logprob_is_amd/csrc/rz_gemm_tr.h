@@ -1,0 +1,328 @@
+// MFMA tile core for the token contraction of the LM-head weight gradient,
+//   C[v][h] = sum_t (e[t][v] 2^-d(t, vt)) hs[t][h],
+// with K = tokens.  Both operands are stored token-major (e in the
+// A-fragment order written by the forward, hs = coef g hhat as [T][H] rows),
+// so the MFMA fragments, which need 8 consecutive tokens per lane, are read
+// from LDS with gfx950's transposing read ds_read_b64_tr_b16: within each
+// group of 16 lanes, lane i receives element i % 4 of the 64-bit words that
+// lanes 4q + i / 4 (q = 0..3) address.  A source lane therefore addresses
+// 4 consecutive values (vocabulary or hidden) of one token; 16 lanes cover 4
+// tokens x 16 values and each lane receives 4 tokens of one value.
+//
+// Tile 256 (vocabulary tile vt) x 256 (hidden tile ht), 4 waves of 128 x 128
+// as in rz_gemm.h, K stages of 64 tokens in a 2-stage LDS ring.  Per stage:
+//  - A: the 32 e fragments (16 vocabulary steps x 2 token blocks of 32) of
+//    the stage, 1 KB each, copied by LDS-direct loads.  Inside a fragment the
+//    16-byte lane slots are permuted on the way in (slot L holds the
+//    forward's lane (L/8)*4 + L%4 + 32 ((L/4) % 2)), so the 16 lanes of one
+//    transposing read touch 128 contiguous bytes; fragments of odd vocabulary
+//    steps also swap their 128-byte halves (slot L ^ 8), so the two 16-lane
+//    groups that the LDS serves together use different banks;
+//  - B: 64 token rows x 256 hidden of hs, as 4-token x 128-hidden pieces
+//    laid out [token/4][hidden half][token%4][16-byte chunk ^ 4 (token%4)]:
+//    each lane quad of a load reads 64 contiguous bytes of one row, and the
+//    XOR spreads a transposing read's 4 tokens over all banks;
+//  - the 64 per-token shifts d(t, vt) << 7 (256 bytes, wave 0 loads them).
+// The exponent shift is applied to the assembled A fragments with a
+// saturating packed 16-bit subtract, as in the P*W^T contraction.
+#pragma once
+
+#include "rz_gemm.h"
+
+namespace rz {
+
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+// ds_read_b64_tr_b16 as inline asm.  Through the compiler builtin every such
+// read is preceded by a wait for all LDS-direct loads in flight (the compiler
+// cannot tell that they fill the other stage buffer), which serialises the
+// pipeline; the asm form carries no such wait, and its results are waited
+// for explicitly (GemmCoreTr::settle) before anything reads them.
+__device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr) {
+  u32x2 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(lds_addr) : "memory");
+  return r;
+}
+
+struct GemmCoreTr {
+  static constexpr int kA = 32768;            // A stage bytes (32 fragments)
+  static constexpr int kB = 32768;            // B stage bytes
+  static constexpr int kD = 256;              // shift bytes per stage
+  static constexpr int kStage = kA + kB + kD;
+  static constexpr int kRing = 2 * kStage;
+
+  __amdgpu_buffer_rsrc_t ra, rb, rd;
+  const char* e_tile0;    // e fragments of (token tile 0, vocabulary step vt*16)
+  int64_t e_tile_stride;  // bytes between token tiles in the e block
+  uint32_t va[2], vb[8];  // per-lane load offsets (A within a fragment, even/odd step; B per piece)
+  char* smem;
+  int wave, nk, a_range, rot;
+  uint32_t rb_stage_bytes;  // 64 token rows of hs
+  uint32_t a_rd[4][2], b_rd[4][2];  // per-lane LDS byte offsets of the tr reads (k-step 0)
+  uint32_t d_rd;                    // LDS offset of the lane's 8 token shifts (k-step 0)
+  f32x16 acc[4][4];
+  u32x4 fa[2][4], fb[2][4];  // fragments (8 bf16 each) as read
+  uint32_t lds_base;         // LDS address of smem
+  u16x8 sh[2];            // per-set exponent shifts (d << 7) of the lane's 8 tokens
+  u32x4 shr[2][2];        // the same as read from LDS (one token per 32-bit word)
+
+  // E: e block of the chunk (fragment order, n_ks = Vp/16 steps); hs: [TC][H]
+  // bf16 rows; D: shift table row of tile vt (d << 7 in the low 16 bits),
+  // at least TCp entries.
+  __device__ __forceinline__ void init(const uint16_t* E, int64_t n_ks, int64_t vt,
+                                       const uint16_t* hs, int64_t TC, int H, int64_t ht,
+                                       const uint32_t* Drow, int64_t TCp, char* lds) {
+    smem = lds;
+    lds_base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
+    const int lane = threadIdx.x & 63;
+    wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
+    const int wm = wave & 1;
+    const int wn = wave >> 1;
+    e_tile0 = reinterpret_cast<const char*>(E) + frag_offset(0, vt * 16, 0, n_ks);
+    e_tile_stride = n_ks * 8 * 1024;
+    rot = __builtin_amdgcn_readfirstlane(int(vt & 3));
+    // the last vocabulary tile may hold fewer than 16 steps (the vocabulary is
+    // padded to 64): its missing fragments read as 0 instead of running into
+    // the next token tile or past the block
+    const int64_t left = n_ks - vt * 16;
+    a_range = int(left < 16 ? left : 16) * 8 * 1024;
+    set_a_tile(0);
+    {
+      const uint64_t p = reinterpret_cast<uint64_t>(hs + ht * kTile);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+      const int n = __builtin_amdgcn_readfirstlane(int(TC * H * 2 - ht * kTile * 2));
+      rb = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                             n, kBufferFlags);
+    }
+    {
+      const uint64_t p = reinterpret_cast<uint64_t>(Drow);
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+      const int n = __builtin_amdgcn_readfirstlane(int(TCp * 4));
+      rd = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                             n, kBufferFlags);
+    }
+    // A: LDS slot L <- forward lane (L/8)*4 + L%4 + 32*((L/4)%2), with
+    // L = lane (even vocabulary step) or lane ^ 8 (odd)
+#pragma unroll
+    for (int o = 0; o < 2; ++o) {
+      const int L = lane ^ (8 * o);
+      va[o] = uint32_t(((L >> 3) << 2) + (L & 3) + 32 * ((L >> 2) & 1)) * 16u;
+    }
+    // B piece q = wave*8 + u: token 4*(q/2) + lane/16, hidden half q%2, LDS
+    // chunk lane%16 <- row chunk (lane%16) ^ 4*(lane/16)
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int q = wave * 8 + u;
+      const int tq = lane >> 4;
+      vb[u] = uint32_t((4 * (q >> 1) + tq) * H * 2 + (q & 1) * 256 + ((lane & 15) ^ (4 * tq)) * 16);
+    }
+    // tr-read addresses for k-step 0 (read_step adds the k-step's offsets)
+    const int g = lane >> 4, s = lane & 15, q = s >> 2, j = s & 3;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // A block i of wave wm: vocabulary step wm*8 + 2i + g%2 of the tile,
+        // token t = 8*(g/2) + 4h + q of the k-step
+        const int ksl = wm * 8 + 2 * i + (g & 1);
+        const int t = 8 * (g >> 1) + 4 * h + q;
+        const int slot = ((t >> 2) * 8 + (j >> 1) * 4 + (t & 3)) ^ (8 * (ksl & 1));
+        a_rd[i][h] = uint32_t(ksl * 2 * 1024 + slot * 16 + 8 * (j & 1));
+        // B block i of wave wn: hidden half wn, chunk 4i + 2(g%2) + j/2
+        const int c = 4 * i + 2 * (g & 1) + (j >> 1);
+        b_rd[i][h] = uint32_t(kA + ((t >> 2) * 2 + wn) * 1024 + (t & 3) * 256 +
+                              (c ^ (4 * (t & 3))) * 16 + 8 * (j & 1));
+      }
+    // the lane's 8 token shifts: tokens 8*(lane/32) .. +7 of the k-step
+    d_rd = uint32_t(kA + kB + (lane >> 5) * 8 * 4);
+    zero_acc(acc);
+  }
+
+  __device__ __forceinline__ void set_a_tile(int64_t tt) {
+    const uint64_t p = reinterpret_cast<uint64_t>(e_tile0 + tt * e_tile_stride);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
+    ra = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(a_range), kBufferFlags);
+  }
+
+  // Token stage (64 tokens) that stage kt covers: the 4 stages of a token
+  // tile are taken in an order rotated by the vocabulary tile, so that
+  // workgroups running side by side read different 2 KB pieces of their e
+  // blocks at the same time (the pieces of one stage lie 8 KB apart).
+  __device__ __forceinline__ int stage_tokens(int kt) const {
+    return (kt & ~3) | (((kt & 3) + rot) & 3);
+  }
+
+  // Loads of stage kt: pair u (0..7) = A fragment and B piece q = wave*8 + u;
+  // wave 0 also loads the stage's shifts with pair 0.
+  __device__ __forceinline__ void load_pair(int kt, int u) {
+    char* s = smem + (kt & 1) * kStage;
+    const int q = wave * 8 + u;
+    const int st = stage_tokens(kt);
+    // A fragment q: vocabulary step q/2, token block 2*(st%4) + q%2 of the tile
+    const int soffA = ((st & 3) * 2) * 1024;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
+                                             uint32_t((q >> 1) * 8192 + (q & 1) * 1024) + va[(u >> 1) & 1],
+                                             soffA, 0, 0);
+    // the whole offset in voffset: rows past TC must fail the range check
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16,
+                                             vb[u] + uint32_t(st) * rb_stage_bytes, 0, 0, 0);
+    if (u == 0 && wave == 0)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(s + kA + kB), 4,
+                                               uint32_t((threadIdx.x & 63) * 4), st * 256, 0, 0);
+  }
+  static __device__ __forceinline__ uint32_t da_of(int kk) {
+    // k-step kk = tokens 16kk .. 16kk+15 of the stage: token block kk/2
+    // (the next 1 KB fragment), rows (kk%2)*16 of it (4 slot groups of 8)
+    return uint32_t((kk >> 1) * 1024 + (kk & 1) * 4 * 8 * 16);
+  }
+  static __device__ __forceinline__ uint32_t db_of(int kk) { return uint32_t(kk * 4 * 2 * 1024); }
+
+  // Read unit u (0..7) of k-step kk into set F: A block u (u < 4) or B block
+  // u - 4, two transposing reads each.
+  template <int F>
+  __device__ __forceinline__ void read_unit(const char* s, int kk, int u) {
+    const uint32_t b = lds_base + uint32_t(s - smem);
+    const uint32_t* rd = u < 4 ? a_rd[u] : b_rd[u - 4];
+    const uint32_t o = u < 4 ? da_of(kk) : db_of(kk);
+    const u32x2 lo = ds_read_tr16(b + rd[0] + o);
+    const u32x2 hi = ds_read_tr16(b + rd[1] + o);
+    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
+    if (u < 4)
+      fa[F][u] = v;
+    else
+      fb[F][u - 4] = v;
+  }
+
+  // Wait for every LDS read in flight, with the set-F fragments as operands
+  // of the wait, so that no use of them can be placed before it.
+  template <int F>
+  __device__ __forceinline__ void settle() {
+    asm volatile("s_waitcnt lgkmcnt(0)"
+                 : "+v"(fa[F][0]), "+v"(fa[F][1]), "+v"(fa[F][2]), "+v"(fa[F][3]),
+                   "+v"(fb[F][0]), "+v"(fb[F][1]), "+v"(fb[F][2]), "+v"(fb[F][3])
+                 :
+                 : "memory");
+    unpack_shift<F>();
+  }
+
+  // The lane's 8 token shifts of k-step kk into set F (as read; unpacked by
+  // unpack_shift once the reads have settled).
+  template <int F>
+  __device__ __forceinline__ void read_shift(const char* s, int kk) {
+    shr[F][0] = *reinterpret_cast<const u32x4*>(s + d_rd + kk * 64);
+    shr[F][1] = *reinterpret_cast<const u32x4*>(s + d_rd + kk * 64 + 16);
+  }
+
+  template <int F>
+  __device__ __forceinline__ void unpack_shift() {
+    u16x8 d;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      d[c] = static_cast<unsigned short>(shr[F][0][c]);
+      d[4 + c] = static_cast<unsigned short>(shr[F][1][c]);
+    }
+    sh[F] = d;
+  }
+
+  template <int F>
+  __device__ __forceinline__ void shift_frag(int i) {
+    fa[F][i] = __builtin_bit_cast(
+        u32x4, __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x8, fa[F][i]), sh[F]));
+  }
+
+  template <int F>
+  __device__ __forceinline__ void mfma_one(int idx) {
+    const int i = idx >> 2, j = idx & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, fa[F][i]),
+                                                        __builtin_bit_cast(bf16x8, fb[F][j]),
+                                                        acc[i][j], 0, 0, 0);
+  }
+
+  // One k-step on set F while reading k-step kk of stage buffer s into set
+  // F^1 (one read unit per MFMA) and, if Load, issuing load pairs
+  // first_pair .. first_pair+3 of stage lkt at MFMAs 0, 4, 8, 12.  A block i
+  // of set F is shifted just before its first MFMA.
+  template <int F, bool Load>
+  __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
+#pragma unroll
+    for (int idx = 0; idx < 16; ++idx) {
+      mfma_one<F>(idx);
+      if (idx < 8) read_unit<F ^ 1>(s, kk, idx);
+      if (idx == 8) read_shift<F ^ 1>(s, kk);
+      if (Load && (idx & 3) == 0) load_pair(lkt, first_pair + (idx >> 2));
+      if ((idx & 3) == 3 && idx < 15) shift_frag<F>((idx >> 2) + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    settle<F ^ 1>();
+    shift_frag<F ^ 1>(0);
+    __builtin_amdgcn_sched_barrier(0);
+  }
+
+  // Stage kt (4 k-steps), whose k-step-0 fragments are in set 0.  If Load,
+  // stage kt+1's loads go out over the first two k-steps; if More, stage
+  // kt+1 is waited for and published in the middle of the last k-step and
+  // its k-step-0 fragments are read during the second half.
+  template <bool Load, bool More>
+  __device__ __forceinline__ void stage(int kt) {
+    const char* s = smem + (kt & 1) * kStage;
+    const int lkt = kt + 1;
+    if (Load && (lkt & 3) == 0) set_a_tile(lkt >> 2);
+    step<0, Load>(s, 1, lkt, 0);
+    step<1, Load>(s, 2, lkt, 4);
+    step<0, false>(s, 3, lkt, 0);
+#pragma unroll
+    for (int idx = 0; idx < 8; ++idx) {
+      mfma_one<1>(idx);
+      if ((idx & 3) == 3) shift_frag<1>((idx >> 2) + 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (More) {
+      GemmCore::wait_loads_except(0);
+      GemmCore::barrier();
+      const char* sn = smem + ((kt + 1) & 1) * kStage;
+#pragma unroll
+      for (int idx = 8; idx < 16; ++idx) {
+        mfma_one<1>(idx);
+        read_unit<0>(sn, 0, idx - 8);
+        if (idx == 11) shift_frag<1>(3);
+        if (idx == 12) read_shift<0>(sn, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      settle<0>();
+      shift_frag<0>(0);
+      __builtin_amdgcn_sched_barrier(0);
+    } else {
+#pragma unroll
+      for (int idx = 8; idx < 16; ++idx) {
+        mfma_one<1>(idx);
+        if (idx == 11) shift_frag<1>(3);
+      }
+    }
+  }
+
+  // K = TCp tokens (a multiple of 256).  Ends with no load in flight and no
+  // LDS read outstanding.
+  __device__ __forceinline__ void run(int K, int H) {
+    rb_stage_bytes = uint32_t(64 * H * 2);
+    nk = K / 64;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) load_pair(0, u);
+    GemmCore::wait_loads_except(0);
+    GemmCore::barrier();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) read_unit<0>(smem, 0, u);
+    read_shift<0>(smem, 0);
+    settle<0>();
+    shift_frag<0>(0);
+    int kt = 0;
+    for (; kt + 1 < nk; ++kt) stage<true, true>(kt);
+    stage<false, false>(kt);
+    GemmCore::barrier();
+  }
+};
+
+}  // namespace rz

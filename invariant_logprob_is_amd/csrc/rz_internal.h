@@ -41,7 +41,7 @@ struct WsLayout {
   // rz_learner_step (chunks of at most kBwdChunk tokens)
   size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_cs, s_lse, s_coef, s_part, step_end;
   // rz_learner_step with weight gradients: the step region, then these
-  size_t g_pt, g_ht, g_ibuf, g_part, grads_end;
+  size_t g_hs, g_ibuf, g_part, grads_end;
   size_t total;
 };
 
@@ -84,8 +84,8 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.s_coef = o; o = align256(o + size_t(T) * 4);
   L.s_part = o; o = align256(o + size_t(T + 8) * 8);
   L.step_end = o;
-  L.g_pt = o;   o = align256(o + size_t(Vp) * tcp * 2);
-  L.g_ht = o;   o = align256(o + size_t(H) * tcp * 2);
+  // the chunk's hhat rows scaled by coef_t g_t (bf16)
+  L.g_hs = o;   o = align256(o + size_t(tc) * H * 2);
   // count, cursor, offsets, bucket slots, sorted order, scan block totals;
   // then the chunk's row factors r_t (float64)
   L.g_ibuf = o; o = align256(o + align256(size_t(3 * V + 1 + 2 * tc + ceil_div(V, 1024) + 1) * 4)
@@ -154,8 +154,8 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                                     const int32_t* target_chunk, const uint16_t* hh,
                                     const uint16_t* x_chunk, float eps, const float* dhh_chunk,
                                     int64_t TC, int H, int V, int64_t gb0, int first,
-                                    uint16_t* Pt, uint16_t* hT, int32_t* ibuf, double* gpart,
-                                    float* dW, hipStream_t s);
+                                    uint16_t* hs, int32_t* ibuf, double* gpart, float* dW,
+                                    hipStream_t s);
 hipError_t launch_dgamma_final(const double* gpart, int64_t nb, int H, float* dgamma,
                                hipStream_t s);
 hipError_t launch_kl(const float* logprob, const float* mu, int64_t T, double* kl,

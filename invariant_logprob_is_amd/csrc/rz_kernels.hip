@@ -4,6 +4,7 @@
 #include <math.h>
 
 #include "rz_gemm.h"
+#include "rz_gemm_tr.h"
 
 namespace rz {
 
@@ -772,95 +773,50 @@ __global__ __launch_bounds__(256) void k_decompose_final(const double* __restric
 // Weight gradients (optional outputs of the learner step).
 //   dW[v] = sum_t coef_t (onehot(target_t)_v - p_tv) hhat_t
 //   dgamma[k] = sum_t dhhat[t, k] x[t, k] r_t
-// The softmax part is a contraction over tokens: Pt[v][t] = coef_t p_tv is
-// formed from the stored e (exact exponent shift, then the factor coef_t g_t
-// in fp32, one rounding to bf16), hhat is transposed, and the same 256x256
-// MFMA tile core computes Pt * hhat^T.  Chunks add into dW in chunk order.
+// The softmax part is a contraction over tokens, sum_t (e_tv 2^-d) hs_t with
+// hs_t = bf16(coef_t g_t hhat_t) (one rounding): the 256x256 MFMA tile core
+// of rz_gemm_tr.h reads e straight from the forward's fragment order with
+// transposing LDS reads and applies the exact exponent shift in registers.
+// Chunks add into dW in chunk order.
 // The one-hot part is added exactly in fp32, per target row in token order,
 // after a deterministic bucketing of the chunk's tokens by target.
 // ---------------------------------------------------------------------------
 
-// Pt[v][t] for a 64 x 64 (vocabulary x token) block: 8 e fragments in, a
-// transpose through LDS, 128-byte row segments out.  Tokens past TC and
-// vocabulary rows past V come out as 0.
-__global__ __launch_bounds__(256) void k_transpose_p(const uint16_t* __restrict__ E,
-                                                     const uint32_t* __restrict__ D, int64_t ds,
-                                                     const float* __restrict__ gf,
-                                                     const float* __restrict__ coef, int64_t TC,
-                                                     int64_t Vp, int64_t TCp,
-                                                     uint16_t* __restrict__ Pt) {
-  __shared__ uint16_t tile[64][66];
-  const int64_t v0 = int64_t(blockIdx.x) * 64;
-  const int64_t t0 = int64_t(blockIdx.y) * 64;
-  const int64_t n_ks = Vp / 16;
-  const int64_t tt = t0 / kTile;
-  const int64_t j = v0 / kTile;                    // vocabulary tile of the whole block
-  const int tid = threadIdx.x;
-  // 8 fragments (4 vocabulary steps x 2 token blocks) x 64 lanes of 16 B:
-  // thread tid takes fragment slot pairs (tid, tid + 256) of the 512.
+// hs[t][h] = bf16(coef_t g_t hhat[t][h]) for the chunk's tokens (the
+// per-token factor of p moved onto the other operand of the token
+// contraction; one rounding).  One wave per row, 8 values per lane step.
+__global__ __launch_bounds__(256) void k_scale_rows(const uint16_t* __restrict__ hh,
+                                                    const float* __restrict__ coef,
+                                                    const float* __restrict__ gf, int64_t TC, int H,
+                                                    uint16_t* __restrict__ hs) {
+  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  if (t >= TC) return;
+  const int lane = threadIdx.x & 63;
+  const float sc = coef[t] * gf[t];
+  for (int c = lane * 8; c < H; c += 64 * 8) {
+    const u32x4 v = *reinterpret_cast<const u32x4*>(hh + t * H + c);
+    u32x4 o;
 #pragma unroll
-  for (int u = 0; u < 2; ++u) {
-    const int q = tid + u * 256;                   // 0..511
-    const int f = q >> 6;                          // fragment 0..7
-    const int lane = q & 63;
-    const int ksl = f >> 1, mbl = f & 1;
-    const int64_t ks = v0 / 16 + ksl;
-    const int64_t mb = (t0 % kTile) / 32 + mbl;
-    const int tl = mbl * 32 + (lane & 31);        // token within the block
-    const int vl = ksl * 16 + 8 * (lane >> 5);     // first vocabulary row within the block
-    const int64_t t = t0 + tl;
-    float sc = 0.0f;
-    uint32_t d = 255u;
-    if (t < TC && ks < n_ks) {
-      sc = coef[t] * gf[t];
-      d = (D[j * ds + t] & 0xFFFFu) >> 7;
-    }
-    u32x4 w = {0u, 0u, 0u, 0u};
-    if (ks < n_ks)
-      w = *reinterpret_cast<const u32x4*>(reinterpret_cast<const char*>(E) +
-                                          frag_offset(tt, ks, mb, n_ks) + lane * 16);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const float e = __uint_as_float(h ? (w[c] & 0xFFFF0000u) : (w[c] << 16));
-        const float p = (d >= 255u) ? 0.0f : ldexpf(e, -int(d)) * sc;
-        tile[vl + 2 * c + h][tl] = f32_to_bf16_rne(p);
-      }
-    }
-  }
-  __syncthreads();
-  const int row = tid >> 2;                        // vocabulary row within the block
-  const int seg = tid & 3;                         // 16-token segment
-  const int64_t v = v0 + row;
-  if (v < Vp) {
-    u32x4 a, b;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      a[c] = uint32_t(tile[row][seg * 16 + 2 * c]) | (uint32_t(tile[row][seg * 16 + 2 * c + 1]) << 16);
-      b[c] = uint32_t(tile[row][seg * 16 + 8 + 2 * c]) |
-             (uint32_t(tile[row][seg * 16 + 8 + 2 * c + 1]) << 16);
-    }
-    uint16_t* dst = Pt + v * TCp + t0 + seg * 16;
-    *reinterpret_cast<u32x4*>(dst) = a;
-    *reinterpret_cast<u32x4*>(dst + 8) = b;
+    for (int q = 0; q < 4; ++q)
+      o[q] = pack_bf16x2(__uint_as_float(v[q] << 16) * sc, __uint_as_float(v[q] & 0xFFFF0000u) * sc);
+    *reinterpret_cast<u32x4*>(hs + t * H + c) = o;
   }
 }
 
-// The softmax part of dW for a chunk: dW[v][h] = (first ? 0 : dW[v][h]) -
-// sum_t Pt[v][t] hT[h][t].  Operand A = Pt (vocabulary rows, K = TCp
-// tokens), operand B = hT (hidden rows).
+// The softmax part of dW straight from the stored e (GemmCoreTr): dW[v][h] =
+// (first ? 0 : dW[v][h]) - sum_t (e_tv 2^-d(t, vt)) hs[t][h].
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void k_dw(const uint16_t* __restrict__ Pt, const uint16_t* __restrict__ hT, int64_t TCp, int H,
-          int V, int64_t n_vt, int64_t n_ht, int first, float* __restrict__ dW) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
+             const uint16_t* __restrict__ hs, int64_t TC, int64_t TCp, int H, int V, int64_t Vp,
+             int64_t n_vt, int64_t n_ht, int first, float* __restrict__ dW) {
+  __shared__ __attribute__((aligned(16))) char lds[GemmCoreTr::kRing];
   int64_t vt, ht;
   if (!tile_of(n_vt, n_ht, vt, ht)) return;
   const int64_t v0 = vt * kTile;
   const int64_t h0 = ht * kTile;
-  GemmCore g;
-  g.init(Pt, v0, V, hT, h0, H, TCp, lds);
-  g.run(int(TCp));
+  GemmCoreTr g;
+  g.init(E, Vp / 16, vt, hs, TC, H, ht, D + vt * ds, TCp, lds);
+  g.run(int(TCp), H);
   f32x16 (&acc)[4][4] = g.acc;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1160,8 +1116,8 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                                     const int32_t* target_chunk, const uint16_t* hh,
                                     const uint16_t* x_chunk, float eps, const float* dhh_chunk,
                                     int64_t TC, int H, int V, int64_t gb0, int first,
-                                    uint16_t* Pt, uint16_t* hT, int32_t* ibuf, double* gpart,
-                                    float* dW, hipStream_t s) {
+                                    uint16_t* hs, int32_t* ibuf, double* gpart, float* dW,
+                                    hipStream_t s) {
   const int64_t Vp = vocab_pad(V);
   const int64_t TCp = shift_stride(TC);
   int32_t* count = ibuf;
@@ -1181,18 +1137,15 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                        s, dhh_chunk, x_chunk, rbuf, TC, H, gb0, gpart);
   }
   {
-    ProfScope prof("k_transpose_p", s);
-    hipLaunchKernelGGL(k_transpose_w, dim3(blocks_for(TCp, 64), H / 64), dim3(256), 0, s, hh, H,
-                       int(TC), TCp, hT);
-    hipLaunchKernelGGL(k_transpose_p, dim3(blocks_for(Vp, 64), uint32_t(TCp / 64)), dim3(256), 0,
-                       s, E, D, ds, g, coef_chunk, TC, Vp, TCp, Pt);
-  }
-  {
+    // hs = coef g hhat (the chunk's rows), then the token contraction
+    // straight from the stored e
     ProfScope prof("k_dw", s);
+    hipLaunchKernelGGL(k_scale_rows, dim3(blocks_for(TC, 4)), dim3(256), 0, s, hh, coef_chunk, g,
+                       TC, H, hs);
     const int64_t n_vt = n_vocab_tiles(V);
     const int64_t n_ht = ceil_div(H, kTile);
-    hipLaunchKernelGGL(k_dw, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, Pt, hT, TCp, H,
-                       V, n_vt, n_ht, first, dW);
+    hipLaunchKernelGGL(k_dw_tr, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, E, D, ds,
+                       hs, TC, TCp, H, V, Vp, n_vt, n_ht, first, dW);
   }
   {
     ProfScope prof("k_onehot", s);
