@@ -29,7 +29,7 @@ PEAK_HBM_BYTES = 8.0e12
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_logprob_is_amd", "csrc", f)
-    for f in ("rz_kernels.hip", "rz_gemm.h", "rz_internal.h")
+    for f in ("rz_kernels.hip", "rz_gemm.h", "rz_gemm_tr.h", "rz_internal.h")
 ]
 
 
@@ -113,12 +113,15 @@ def summarize_counters(fetch_csv: str, write_csv: str):
     cw = max(write.get(copy, [0.0])) / CALIBRATION_BYTES
     os.makedirs(PROFILES, exist_ok=True)
     sha = source_sha()
-    # the learner step launches the storing forward variant
-    for k, disp in (("k_lmhead_fwd", "k_lmhead_fwd<true>"), ("k_dhidden", "k_dhidden")):
-        if disp not in fetch or disp not in write:
+    # the learner step launches the storing forward variant; k_dw (--grads)
+    # is the row scaling plus the token contraction, one of each per chunk
+    for k, disps in (("k_lmhead_fwd", ("k_lmhead_fwd<true>",)), ("k_dhidden", ("k_dhidden",)),
+                     ("k_dw", ("k_scale_rows", "k_dw_tr"))):
+        if any(d not in fetch or d not in write for d in disps):
             continue
-        f = float(np.mean(fetch[disp])) / (cf or 1.0)
-        w = float(np.mean(write[disp])) / (cw or 1.0)
+        disp = disps[-1]
+        f = sum(float(np.mean(fetch[d])) for d in disps) / (cf or 1.0)
+        w = sum(float(np.mean(write[d])) for d in disps) / (cw or 1.0)
         d = {"kernel": k, "source_sha": sha, "bytes_per_launch": f + w,
              "fetch_bytes_per_launch": f, "write_bytes_per_launch": w,
              "launches": len(fetch[disp]), "calibration": {
