@@ -208,6 +208,77 @@ def probe(args, b, rz, x, g, W, tgt, lp, ws, stream):
     }), flush=True)
 
 
+def shards(args, b, rz, x, g, W, tgt, lp, lse, ws):
+    """The log-probabilities of the workload through `args.shards` equal
+    shares of the vocabulary splits (rz_logprob_shard on each share's rows of
+    W, one share after another on this GPU) and the merge (rz_logprob_merge).
+    Each share's time is what one device of a vocabulary-parallel head would
+    spend on it; the merged bits are checked against rz_logprob's."""
+    import torch
+
+    dev = x.device
+    T, H, V = b.T, b.H, b.V
+    d = args.shards
+    k = rz.VOCAB_SPLITS // d
+    plan = [(r * k, (r + 1) * k) for r in range(d)]
+    rows = [(rz.vocab_split_begin(V, s0), rz.vocab_split_begin(V, s1)) for s0, s1 in plan]
+    parts = torch.empty((rz.VOCAB_SPLITS, T, 3), dtype=torch.float64, device=dev)
+    mlp = torch.empty(T, dtype=torch.float32, device=dev)
+    mlse = torch.empty(T, dtype=torch.float32, device=dev)
+
+    def call(ev=None):
+        for r, ((s0, s1), (a, c)) in enumerate(zip(plan, rows)):
+            if ev:
+                ev[r][0].record()
+            rz.logprob_shard(x, g, W[a:c], tgt, V, s0, s1, b.eps, workspace=ws,
+                             out=parts[s0:s1])
+            if ev:
+                ev[r][1].record()
+        if ev:
+            ev[d][0].record()
+        rz.logprob_merge(parts, tgt, V, out=mlp, lse_out=mlse)
+        if ev:
+            ev[d][1].record()
+
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    same = bool(torch.equal(mlp.view(torch.int32), lp.view(torch.int32)) and
+                torch.equal(mlse.view(torch.int32), lse.view(torch.int32)))
+    per = np.zeros(d + 1)
+    rz.profile_enable(True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(d + 1)]
+        call(ev)
+        torch.cuda.synchronize()
+        per += [a.elapsed_time(c) for a, c in ev]
+    wall = time.perf_counter() - t0
+    prof = rz.profile_read()
+    rz.profile_enable(False)
+    per /= args.steps
+    ms = 1000.0 * wall / args.steps
+    log(f"{d} shares: {ms:.2f} ms per pass; shares {np.round(per[:d], 2).tolist()} ms, "
+        f"merge {per[d]:.3f} ms; bits equal to rz_logprob: {same}")
+    if not same:
+        raise SystemExit("sharded logprob differs from rz_logprob")
+    tot, n = prof["k_lmhead_fwd"]
+    achieved = 2.0 * T * H * V * args.steps / (tot / 1000.0)
+    print(json.dumps({
+        "metric": "vocab-split logprob tokens/sec (all shares in turn + merge), 1 GPU",
+        "value": T / (ms / 1000.0), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}; vocabulary in {d} shares "
+                               f"of {k} splits", "T": T, "H": H, "V": V, "shares": d},
+        "share_ms": per[:d].tolist(), "merge_ms": float(per[d]), "bits_equal_rz_logprob": same,
+        "roofline": {"kernel": "k_lmhead_fwd", "bound": "mfma", "achieved": achieved / 1e12,
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": achieved / PEAK_BF16_FLOPS, "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -223,6 +294,9 @@ def main():
     ap.add_argument("--probe", action="store_true",
                     help="time the log-ratio decomposition probe (rz_decompose) and track the KL "
                          "estimators over synthetic updates instead of the learner step")
+    ap.add_argument("--shards", type=int, choices=[1, 2, 4, 8],
+                    help="time the log-probabilities through this many equal shares of the "
+                         "vocabulary splits and their merge instead of the learner step")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/traffic_<kernel>.json and exit")
@@ -282,6 +356,9 @@ def main():
     torch.cuda.synchronize()
     if args.probe:
         probe(args, b, rz, x, g, W, tgt, lp, ws, stream)
+        return
+    if args.shards:
+        shards(args, b, rz, x, g, W, tgt, lp, lse, ws)
         return
 
     def step():

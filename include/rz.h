@@ -142,6 +142,75 @@ RZ_API int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
  * Errors: RZ_EINVAL (null pointer, T < 1, R < 1, G < 1, R > T, G > R),
  * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
+/*
+ * Vocabulary splits -- rz_logprob's log-sum-exp is combined in two fixed
+ * levels: over the 256-row vocabulary tiles of each of RZ_VOCAB_SPLITS
+ * splits, then over the splits, each in order.  Split s covers the tiles
+ * [s n / RZ_VOCAB_SPLITS, (s+1) n / RZ_VOCAB_SPLITS), n = ceil(V / 256): a
+ * function of V alone.  A device that holds the rows of any whole number of
+ * consecutive splits of W can therefore produce those splits' partials
+ * (rz_logprob_shard), and the merge of all splits (rz_logprob_merge) gives
+ * logprob and lse bit for bit equal to rz_logprob's, whatever the number of
+ * devices the vocabulary was spread over (1, 2, 4 or 8 equal shares).  This
+ * is the fixed-order reduction that keeps a vocabulary-parallel head at zero
+ * difference across device counts ([P2] "Large-model validation exposes
+ * concrete failure mechanisms": zero difference on a multi-node run, with
+ * arrival-ordered reductions named as a source of batch variance).
+ */
+#define RZ_VOCAB_SPLITS 8
+
+/* One row's partial of one split (24 bytes, 8-byte aligned). */
+typedef struct rz_vocab_split {
+  double s;          /* sum over the split's tiles j of S_j 2^(m_j - m), in tile order */
+  float m;           /* the split's reference exponent max_j m_j (integer-valued; -inf if empty) */
+  float max_logit;   /* max over the split's rows of z_tv (-inf if empty) */
+  float z_target;    /* z_{t, target[t]} if target[t] lies in the split, else 0 */
+  float reserved;    /* 0 */
+} rz_vocab_split;
+/* (S_j = sum over tile j's rows of 2^(z_tv log2 e - m_j), m_j =
+ *  ceil(max_v z_tv log2 e), both computed as in rz_logprob.) */
+
+/*
+ * rz_vocab_split_begin -- first vocabulary row of split s (0 <= s <=
+ * RZ_VOCAB_SPLITS; s = RZ_VOCAB_SPLITS gives V).  The rows of splits
+ * [s0, s1) are [rz_vocab_split_begin(V, s0), rz_vocab_split_begin(V, s1)).
+ * Returns -1 for V < 1, V > 4000000 or s out of range.  Host only.
+ */
+RZ_API int64_t rz_vocab_split_begin(int32_t V, int32_t s);
+
+/*
+ * rz_logprob_shard -- the partials of splits [s0, s1) of every row.
+ *
+ * W_rows points at row rz_vocab_split_begin(V, s0) of the [V,H] weight and
+ * holds the rows of splits s0 .. s1-1 (row-major, as in W).  x, gamma, eps,
+ * target (global row indices), T, H, V as for rz_logprob.  partials
+ * [(s1 - s0), T] out: partials[(s - s0) * T + t] is split s's record of row
+ * t.  workspace as rz_logprob (rz_workspace_bytes(T, H, V)).
+ * Errors: RZ_EINVAL (null pointer, misalignment, not 0 <= s0 < s1 <=
+ * RZ_VOCAB_SPLITS), and those of rz_logprob.
+ */
+RZ_API int rz_logprob_shard(const uint16_t* x, const uint16_t* gamma, float eps,
+                            const uint16_t* W_rows, const int32_t* target,
+                            int64_t T, int32_t H, int32_t V, int32_t s0, int32_t s1,
+                            rz_vocab_split* partials,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_logprob_merge -- logprob and lse from the records of all splits.
+ *
+ * partials [RZ_VOCAB_SPLITS, T] (split-major, as rz_logprob_shard writes
+ * them: the blocks of consecutive shards simply follow each other); target
+ * [T] int32 (a target outside [0, V) gives NaN, as in rz_logprob); logprob
+ * [T] fp32 out; lse [T] fp32 out, may be NULL.  With m = max_s m_s:
+ *   lse = max(m ln 2 + log sum_s s_s 2^(m_s - m), max_s max_logit_s)
+ * in fp64 and split order; logprob = sum_s z_target_s - lse.  Needs no
+ * workspace.
+ * Errors: RZ_EINVAL (null pointer, misalignment, T < 1, V < 1,
+ * V > 4000000), RZ_ENODEV, RZ_EHIP.
+ */
+RZ_API int rz_logprob_merge(const rz_vocab_split* partials, const int32_t* target,
+                            int64_t T, int32_t V, float* logprob, float* lse, void* stream);
+
 RZ_API int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
                const int64_t* resp_offsets, int32_t R,
                const int64_t* group_offsets, int32_t G,

@@ -22,6 +22,7 @@ from typing import Optional
 __all__ = [
     "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "logprob", "is_loss", "d3", "kl",
     "decompose", "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH",
+    "VOCAB_SPLITS", "vocab_split_begin", "logprob_shard", "logprob_merge", "split_records",
     "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
 ]
@@ -29,6 +30,9 @@ __all__ = [
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librz.so")
 
 RZ_OK, RZ_EINVAL, RZ_EUNSUPPORTED, RZ_ENODEV, RZ_EHIP, RZ_EWORKSPACE = range(6)
+
+VOCAB_SPLITS = 8        # RZ_VOCAB_SPLITS
+_SPLIT_RECORD = 24      # sizeof(rz_vocab_split)
 
 _P = ctypes.c_void_p
 _I64 = ctypes.c_int64
@@ -52,6 +56,10 @@ SYMBOLS = {
     "rz_learner_step": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _I64, _I32, _I32, _P, _I32, _P,
                                        _I32, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, _SZ,
                                        _P]),
+    "rz_vocab_split_begin": (_I64, [_I32, _I32]),
+    "rz_logprob_shard": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _I32, _I32, _P,
+                                        _P, _SZ, _P]),
+    "rz_logprob_merge": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
     "rz_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "rz_profile_count": (ctypes.c_int, []),
     "rz_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),
@@ -163,6 +171,83 @@ def logprob(x, gamma, W, target, eps: float = 1e-6, *, workspace=None, out=None,
                           ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_logprob", st)
     return lp, ls
+
+
+def vocab_split_begin(V: int, s: int) -> int:
+    """First vocabulary row of split s (rz_vocab_split_begin); s = VOCAB_SPLITS gives V."""
+    r = int(lib().rz_vocab_split_begin(V, s))
+    if r < 0:
+        raise ValueError(f"invalid split {s} for V = {V}")
+    return r
+
+
+def logprob_shard(x, gamma, W_rows, target, V: int, s0: int, s1: int, eps: float = 1e-6, *,
+                  workspace=None, out=None):
+    """Partials of vocabulary splits [s0, s1) (rz_logprob_shard).
+
+    W_rows holds rows [vocab_split_begin(V, s0), vocab_split_begin(V, s1)) of
+    the [V,H] weight (a view of W, or a device's own share of it).  Returns
+    the records as a [s1 - s0, T, 3] float64 tensor holding rz_vocab_split
+    structs (decode with split_records)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W_rows, "W_rows", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    if not (0 <= s0 < s1 <= VOCAB_SPLITS):
+        raise ValueError(f"need 0 <= s0 < s1 <= {VOCAB_SPLITS}")
+    rows = vocab_split_begin(V, s1) - vocab_split_begin(V, s0)
+    if W_rows.shape != (rows, H) and not (rows == 0 and W_rows.shape[1] == H):
+        raise ValueError(f"W_rows must hold the {rows} rows of splits [{s0}, {s1})")
+    if gamma.shape[0] != H or target.shape[0] != T:
+        raise ValueError("shape mismatch among x, gamma, target")
+    recs = out if out is not None else torch.empty((s1 - s0, T, 3), dtype=torch.float64,
+                                                   device=dev)
+    _need(recs, "out", torch.float64, dev, 3)
+    if tuple(recs.shape) != (s1 - s0, T, 3):
+        raise ValueError("out must be [s1 - s0, T, 3] float64")
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    # an empty share still needs a valid, aligned pointer
+    wp = W_rows.data_ptr() if W_rows.numel() else gamma.data_ptr()
+    st = lib().rz_logprob_shard(x.data_ptr(), gamma.data_ptr(), float(eps), wp,
+                                target.data_ptr(), T, H, V, s0, s1, recs.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_logprob_shard", st)
+    return recs
+
+
+def logprob_merge(partials, target, V: int, *, out=None, lse_out=None):
+    """logprob and lse from the records of all splits (rz_logprob_merge).
+
+    partials: [VOCAB_SPLITS, T, 3] float64 (the shards' outputs concatenated
+    in split order).  Returns (logprob [T] fp32, lse [T] fp32)."""
+    torch = _torch()
+    dev = partials.device
+    _need(partials, "partials", torch.float64, dev, 3)
+    _need(target, "target", torch.int32, dev, 1)
+    T = target.shape[0]
+    if tuple(partials.shape) != (VOCAB_SPLITS, T, 3):
+        raise ValueError(f"partials must be [{VOCAB_SPLITS}, T, 3] float64")
+    lp = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    ls = lse_out if lse_out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    _need(lp, "out", torch.float32, dev, 1)
+    _need(ls, "lse_out", torch.float32, dev, 1)
+    st = lib().rz_logprob_merge(partials.data_ptr(), target.data_ptr(), T, V, lp.data_ptr(),
+                                ls.data_ptr(), _stream(dev))
+    _check("rz_logprob_merge", st)
+    return lp, ls
+
+
+def split_records(partials):
+    """Host copy of split records as a numpy structured array with fields
+    s (f8), m, max_logit, z_target, reserved (f4)."""
+    import numpy as np
+    raw = partials.detach().cpu().contiguous().numpy().view(np.uint8)
+    dt = np.dtype([("s", "<f8"), ("m", "<f4"), ("max_logit", "<f4"), ("z_target", "<f4"),
+                   ("reserved", "<f4")])
+    return raw.reshape(-1).view(dt).reshape(partials.shape[:-1])
 
 
 def validate_offsets(resp_offsets, group_offsets, T: int):

@@ -60,6 +60,30 @@ hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, cons
   return e;
 }
 
+// The forward of rz_logprob over the rows of splits [s0, s1) (W points at
+// the first of them), reduced to one record per split and row.
+hipError_t run_shard(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                     const int32_t* target, int64_t T, int32_t H, int32_t V, int s0, int s1,
+                     void* partials, void* workspace, const WsLayout& L, hipStream_t s) {
+  uint16_t* hhat = at<uint16_t>(workspace, L.hhat);
+  float* pm = at<float>(workspace, L.pm);
+  float* ps = at<float>(workspace, L.ps);
+  float* zt = at<float>(workspace, L.ztgt);
+  const int64_t v0 = split_first_row(V, s0);
+  const int Vs = int(split_first_row(V, s1) - v0);
+  hipError_t e = hipSuccess;
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, s);
+    if (e == hipSuccess)
+      e = launch_lmhead_fwd_range(hhat, W, target + c0, tc, H, v0, Vs, pm, ps, zt, s);
+    if (e == hipSuccess)
+      e = launch_split_partials(pm, ps, zt, target + c0, tc, V, s0, s1,
+                                static_cast<char*>(partials) + c0 * sizeof(rz_vocab_split), T, s);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -106,6 +130,48 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
 
   return status_of(run_logprob(x, gamma, eps, W, target, T, H, V, logprob, lse, workspace, L,
                                static_cast<hipStream_t>(stream)));
+}
+
+static_assert(RZ_VOCAB_SPLITS == kVocabSplits, "split count");
+static_assert(sizeof(rz_vocab_split) == 24 && alignof(rz_vocab_split) == 8, "record layout");
+
+int64_t rz_vocab_split_begin(int32_t V, int32_t s) {
+  if (V < 1 || int64_t(V) > kMaxV || s < 0 || s > RZ_VOCAB_SPLITS) return -1;
+  return split_first_row(V, s);
+}
+
+int rz_logprob_shard(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W_rows,
+                     const int32_t* target, int64_t T, int32_t H, int32_t V, int32_t s0,
+                     int32_t s1, rz_vocab_split* partials, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!x || !gamma || !W_rows || !target || !partials || !workspace) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W_rows) || !aligned4(target) ||
+      (reinterpret_cast<uintptr_t>(partials) & 7u) ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  if (s0 < 0 || s1 <= s0 || s1 > RZ_VOCAB_SPLITS) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  const WsLayout L = ws_layout(T, H, V);
+  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  return status_of(run_shard(x, gamma, eps, W_rows, target, T, H, V, s0, s1, partials, workspace,
+                             L, static_cast<hipStream_t>(stream)));
+}
+
+int rz_logprob_merge(const rz_vocab_split* partials, const int32_t* target, int64_t T, int32_t V,
+                     float* logprob, float* lse, void* stream) {
+  if (!partials || !target || !logprob) return RZ_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(partials) & 7u) || !aligned4(target) || !aligned4(logprob) ||
+      (lse && !aligned4(lse)))
+    return RZ_EINVAL;
+  if (T < 1 || V < 1 || int64_t(V) > kMaxV) return RZ_EINVAL;
+  const int st = check_device();
+  if (st != RZ_OK) return st;
+  return status_of(launch_split_merge(partials, T, target, T, V, logprob, lse,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,

@@ -25,6 +25,18 @@ inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }
 
 inline int64_t n_vocab_tiles(int64_t V) { return ceil_div(V, kTile); }
 inline int64_t vocab_pad(int64_t V) { return round_up(V, kBK); }
+// Vocabulary splits: the log-sum-exp of a row is combined in two fixed
+// levels, over the 256-row tiles of each split and then over the splits, in
+// order.  Split s covers tiles [s n_vt / kVocabSplits, (s+1) n_vt /
+// kVocabSplits), a function of V alone, so a device that holds any whole
+// number of splits of W produces the same per-split partials and every
+// merge gives the same bits.
+constexpr int kVocabSplits = 8;
+inline int64_t split_first_tile(int64_t V, int s) { return n_vocab_tiles(V) * s / kVocabSplits; }
+inline int64_t split_first_row(int64_t V, int s) {
+  const int64_t r = split_first_tile(V, s) * kTile;
+  return r < V ? r : V;
+}
 // Row stride of the per-tile shift table of a chunk of tc tokens: whole
 // 256-row token tiles, so the contraction reads it without a bounds check.
 inline int64_t shift_stride(int64_t tc) { return round_up(tc, kTile); }
@@ -128,6 +140,22 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float ep
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
                              uint16_t* E, hipStream_t s);
+// The forward over the vocabulary rows [v0, v0 + Vs) of a model with V rows
+// in all (W points at row v0; targets are global row indices).  ztgt starts
+// at 0: only rows whose target lies in the range get their logit.
+hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
+                                   int64_t T, int H, int64_t v0, int Vs, float* pm, float* ps,
+                                   float* ztgt, hipStream_t s);
+// Per-split records (struct rz_vocab_split of rz.h) for splits [s0, s1) of a
+// model with V rows, from the tile partials of the range forward above
+// (whose first tile is split s0's); out[(s - s0) * out_stride + t].
+hipError_t launch_split_partials(const float* pm, const float* ps, const float* ztgt,
+                                 const int32_t* target, int64_t T, int V, int s0, int s1,
+                                 void* out, int64_t out_stride, hipStream_t s);
+// logprob and lse from all kVocabSplits records of each row (the same
+// arithmetic as launch_lse_combine).
+hipError_t launch_split_merge(const void* parts, int64_t part_stride, const int32_t* target,
+                              int64_t T, int V, float* logprob, float* lse, hipStream_t s);
 hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztgt,
                               int64_t T, int V, float* logprob, float* lse, const double* cs,
                               const float* mu, float* coef, uint32_t* D, int64_t ds, float* g,

@@ -299,7 +299,7 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
 template <bool Store>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
-                  const int32_t* __restrict__ target, int64_t T, int H, int V,
+                  const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
                   int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
                   float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
   __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
@@ -323,12 +323,13 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   const int half = lane >> 5;
   const int64_t vbase = v0 + wm * 128;
 
-  // Target gather: exactly one lane of one workgroup holds z[t, target[t]].
+  // Target gather: exactly one lane of one workgroup holds z[t, target[t]]
+  // (target rows relative to W's first row).
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int64_t t = t0 + acc_col(wn, j, lane);
     if (t < T) {
-      const int64_t tg = target[t];
+      const int64_t tg = int64_t(target[t]) - tgt_off;
       const int64_t loc = tg - vbase;
       if (tg >= 0 && tg < V && loc >= 0 && loc < 128) {
         const int q = int(loc & 31);
@@ -381,11 +382,77 @@ __device__ __forceinline__ float max_tile_max(const float* __restrict__ pm, int6
   return M;
 }
 
-// Merge the per-tile partials (M_j, S_j) of each token in vocabulary-tile
-// order, in float64: with m_j = tile_ref(M_j) and m = max_j m_j,
-// lse = max(m ln 2 + log sum_j S_j 2^(m_j - m), max_j M_j) (the max keeps
-// lse >= every logit against the rounding of the S_j), logprob =
-// z_target - lse.  If cs is given (learner step), also
+// One vocabulary split's partial of a row, over its tiles j0 .. j1-1 in
+// order, in float64: mx = max_j M_j, m = tile_ref(mx) (= max_j m_j, since
+// tile_ref is monotone) and s = sum_j S_j 2^(m_j - m).  An empty split (or
+// one whose tiles are all -inf) gives s = 0, m = mx = -inf.
+struct SplitPart {
+  double s;
+  float m, mx;
+};
+
+__device__ __forceinline__ SplitPart split_part(const float* __restrict__ pm,
+                                                const float* __restrict__ ps, int64_t T,
+                                                int64_t t, int64_t j0, int64_t j1) {
+  // Loads go out kU at a time (the loops are latency bound); the reductions
+  // still run j = j0, j0+1, ... one after another.
+  constexpr int kU = 8;
+  float mx = -INFINITY;
+  int64_t j = j0;
+  for (; j + kU <= j1; j += kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = pm[(j + u) * T + t];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mx = fmaxf(mx, v[u]);
+  }
+  for (; j < j1; ++j) mx = fmaxf(mx, pm[j * T + t]);
+  const float m = tile_ref(mx);
+  double sum = 0.0;
+  j = j0;
+  for (; j + kU <= j1; j += kU) {
+    float mj[kU], sj[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      mj[u] = pm[(j + u) * T + t];
+      sj[u] = ps[(j + u) * T + t];
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u)
+      if (mj[u] != -INFINITY)
+        sum += ldexp(double(sj[u]), int(fmaxf(tile_ref(mj[u]) - m, -4096.0f)));
+  }
+  for (; j < j1; ++j) {
+    const float mj = pm[j * T + t];
+    if (mj != -INFINITY)
+      sum += ldexp(double(ps[j * T + t]), int(fmaxf(tile_ref(mj) - m, -4096.0f)));
+  }
+  return {sum, m, mx};
+}
+
+// Merge of a row's kVocabSplits split partials, in split order, in float64:
+// with m = max_s m_s, lse = max(m ln 2 + log sum_s s_s 2^(m_s - m), max_s mx_s)
+// (the max keeps lse >= every logit against the rounding of the sums).
+// part(s) returns split s's partial; m is returned for the shift table.
+template <class Part>
+__device__ __forceinline__ double merge_splits(Part part, float& m_out) {
+  float m = -INFINITY, mx = -INFINITY;
+#pragma unroll
+  for (int q = 0; q < kVocabSplits; ++q) {
+    m = fmaxf(m, part(q).m);
+    mx = fmaxf(mx, part(q).mx);
+  }
+  double sum = 0.0;
+#pragma unroll
+  for (int q = 0; q < kVocabSplits; ++q)
+    if (part(q).m != -INFINITY) sum += ldexp(part(q).s, int(fmaxf(part(q).m - m, -4096.0f)));
+  m_out = m;
+  return fmax(double(m) * kLn2 + log(sum), double(mx));
+}
+
+// The log-sum-exp of each token from its per-tile partials (M_j, S_j): split
+// partials over each split's tiles, then their merge (both in order),
+// logprob = z_target - lse.  If cs is given (learner step), also
 // coef = cs * exp(logprob - mu), the same expression rz_is_loss evaluates,
 // and if D is given the shift table and row factor of the stored e.
 __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ pm,
@@ -400,36 +467,74 @@ __global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ p
                                                      float* __restrict__ g) {
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= T) return;
-  // Both passes keep several loads in flight (the loop is latency bound);
-  // the summation order is j = 0, 1, 2, ... regardless.
-  const float Mx = max_tile_max(pm, T, n_vt, t);
-  const float m = tile_ref(Mx);
-  double s = 0.0;
-  constexpr int kU = 8;
-  int64_t j = 0;
-  for (; j + kU <= n_vt; j += kU) {
-    float mj[kU], sj[kU];
+  SplitPart P[kVocabSplits];
 #pragma unroll
-    for (int u = 0; u < kU; ++u) {
-      mj[u] = pm[(j + u) * T + t];
-      sj[u] = ps[(j + u) * T + t];
-    }
-#pragma unroll
-    for (int u = 0; u < kU; ++u)
-      if (mj[u] != -INFINITY)
-        s += ldexp(double(sj[u]), int(fmaxf(tile_ref(mj[u]) - m, -4096.0f)));
-  }
-  for (; j < n_vt; ++j) {
-    const float mj = pm[j * T + t];
-    if (mj != -INFINITY) s += ldexp(double(ps[j * T + t]), int(fmaxf(tile_ref(mj) - m, -4096.0f)));
-  }
-  const double l = fmax(double(m) * kLn2 + log(s), double(Mx));
+  for (int q = 0; q < kVocabSplits; ++q)
+    P[q] = split_part(pm, ps, T, t, n_vt * q / kVocabSplits, n_vt * (q + 1) / kVocabSplits);
+  float m;
+  const double l = merge_splits([&](int q) -> const SplitPart& { return P[q]; }, m);
   const float lp = float(double(ztgt[t]) - l);
   const float lf = float(l);
   logprob[t] = lp;
   if (lse) lse[t] = lf;
   if (cs) coef[t] = float(cs[t] * exp(double(lp) - double(mu[t])));
   if (D) shift_tables(pm, T, n_vt, t, m, lf, D, ds, g);
+}
+
+// One row's record of one vocabulary split (struct rz_vocab_split).
+struct SplitRec {
+  double s;
+  float m, mx, z, pad;
+};
+static_assert(sizeof(SplitRec) == 24, "record layout");
+
+// Records of splits [s0, s1) of a model with n_vt vocabulary tiles and V
+// rows, from the tile partials of a forward over those splits' rows (its
+// tile 0 is split s0's first tile).  z is the target logit in the split
+// that holds the target row and 0 in the others.
+__global__ __launch_bounds__(256) void k_split_partials(const float* __restrict__ pm,
+                                                        const float* __restrict__ ps,
+                                                        const float* __restrict__ ztgt,
+                                                        const int32_t* __restrict__ target,
+                                                        int64_t T, int V, int64_t n_vt, int s0,
+                                                        int s1, SplitRec* __restrict__ out,
+                                                        int64_t out_stride) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  const int64_t jb = n_vt * s0 / kVocabSplits;
+  const int64_t tg = target[t];
+  for (int q = s0; q < s1; ++q) {
+    const int64_t j0 = n_vt * q / kVocabSplits, j1 = n_vt * (q + 1) / kVocabSplits;
+    const SplitPart p = split_part(pm, ps, T, t, j0 - jb, j1 - jb);
+    const bool owner = tg >= j0 * kTile && tg < j1 * kTile && tg < V;
+    out[(q - s0) * out_stride + t] = {p.s, p.m, p.mx, owner ? ztgt[t] : 0.0f, 0.0f};
+  }
+}
+
+// logprob and lse of each row from all of its split records: the merge of
+// k_lse_combine, z = the sum of the records' z (one of them is the target
+// logit), NaN for a target outside [0, V).
+__global__ __launch_bounds__(256) void k_split_merge(const SplitRec* __restrict__ parts,
+                                                     int64_t part_stride,
+                                                     const int32_t* __restrict__ target,
+                                                     int64_t T, int V, float* __restrict__ logprob,
+                                                     float* __restrict__ lse) {
+  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (t >= T) return;
+  SplitPart P[kVocabSplits];
+  float z = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kVocabSplits; ++q) {
+    const SplitRec r = parts[q * part_stride + t];
+    P[q] = {r.s, r.m, r.mx};
+    z += r.z;
+  }
+  const int32_t tg = target[t];
+  if (tg < 0 || tg >= V) z = NAN;
+  float m;
+  const double l = merge_splits([&](int q) -> const SplitPart& { return P[q]; }, m);
+  logprob[t] = float(double(z) - l);
+  if (lse) lse[t] = float(l);
 }
 
 // The same shift table and row factor from a given lse (stand-alone backward).
@@ -1031,10 +1136,44 @@ hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int3
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, NAN);
   if (E)
     hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
-                       hhat, W, target, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E);
+                       hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
+                       ztgt, E);
   else
     hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
-                       hhat, W, target, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E);
+                       hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
+                       ztgt, E);
+  return hipGetLastError();
+}
+
+hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
+                                   int64_t T, int H, int64_t v0, int Vs, float* pm, float* ps,
+                                   float* ztgt, hipStream_t s) {
+  ProfScope prof("k_lmhead_fwd", s);
+  const int64_t n_vt = n_vocab_tiles(Vs);
+  const int64_t n_tt = ceil_div(T, kTile);
+  hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, 0.0f);
+  if (n_vt > 0)
+    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+                       hhat, W, target, v0, T, H, Vs, n_vt, n_tt, vocab_pad(Vs), pm, ps, ztgt,
+                       static_cast<uint16_t*>(nullptr));
+  return hipGetLastError();
+}
+
+hipError_t launch_split_partials(const float* pm, const float* ps, const float* ztgt,
+                                 const int32_t* target, int64_t T, int V, int s0, int s1,
+                                 void* out, int64_t out_stride, hipStream_t s) {
+  ProfScope prof("k_lse_combine", s);
+  hipLaunchKernelGGL(k_split_partials, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, ps, ztgt,
+                     target, T, V, n_vocab_tiles(V), s0, s1, static_cast<SplitRec*>(out),
+                     out_stride);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_merge(const void* parts, int64_t part_stride, const int32_t* target,
+                              int64_t T, int V, float* logprob, float* lse, hipStream_t s) {
+  ProfScope prof("k_lse_combine", s);
+  hipLaunchKernelGGL(k_split_merge, dim3(blocks_for(T, 256)), dim3(256), 0, s,
+                     static_cast<const SplitRec*>(parts), part_stride, target, T, V, logprob, lse);
   return hipGetLastError();
 }
 

@@ -220,6 +220,51 @@ def test_learner_step_argument_validation():
     assert _step(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
 
 
+def test_vocab_split_boundaries():
+    # split s starts at tile floor(s * n / 8), n = ceil(V / 256), clipped to V
+    L = rz.lib()
+    for V in (1, 65, 255, 256, 257, 513, 3000, 151936, 4000000):
+        n = -(-V // 256)
+        want = [min(n * s // 8 * 256, V) for s in range(9)]
+        assert [L.rz_vocab_split_begin(V, s) for s in range(9)] == want
+        assert want[0] == 0 and want[-1] == V and want == sorted(want)
+    assert L.rz_vocab_split_begin(151936, 1) == 74 * 256
+    assert L.rz_vocab_split_begin(0, 0) == -1
+    assert L.rz_vocab_split_begin(4000001, 0) == -1
+    assert L.rz_vocab_split_begin(100, -1) == -1
+    assert L.rz_vocab_split_begin(100, 9) == -1
+
+
+def _shard(**kw):
+    a = dict(x=FAKE, g=FAKE, eps=1e-6, W=FAKE, target=FAKE, T=300, H=128, V=1024, s0=0, s1=8,
+             parts=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_logprob_shard(a["x"], a["g"], a["eps"], a["W"], a["target"], a["T"],
+                                     a["H"], a["V"], a["s0"], a["s1"], a["parts"], a["ws"],
+                                     a["wsb"], a["stream"])
+
+
+def test_shard_and_merge_argument_validation():
+    for k in ("x", "g", "W", "target", "parts", "ws"):
+        assert _shard(**{k: None}) == rz.RZ_EINVAL, k
+    assert _shard(parts=FAKE + 4) == rz.RZ_EINVAL          # records are 8-byte aligned
+    assert _shard(W=FAKE + 8) == rz.RZ_EINVAL
+    assert _shard(eps=-1.0) == rz.RZ_EINVAL
+    for s0, s1 in ((0, 0), (3, 2), (-1, 4), (0, 9), (8, 8)):
+        assert _shard(s0=s0, s1=s1) == rz.RZ_EINVAL, (s0, s1)
+    assert _shard(T=0) == rz.RZ_EINVAL
+    assert _shard(H=100) == rz.RZ_EUNSUPPORTED
+    assert _shard(wsb=rz.workspace_bytes(300, 128, 1024) - 1) == rz.RZ_EWORKSPACE
+    L = rz.lib()
+    assert L.rz_logprob_merge(None, FAKE, 10, 100, FAKE, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE, None, 10, 100, FAKE, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE, FAKE, 10, 100, None, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE + 4, FAKE, 10, 100, FAKE, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE, FAKE, 0, 100, FAKE, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE, FAKE, 10, 0, FAKE, FAKE, None) == rz.RZ_EINVAL
+    assert L.rz_logprob_merge(FAKE, FAKE, 10, 4000001, FAKE, FAKE, None) == rz.RZ_EINVAL
+
+
 @pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
 def test_no_device_is_reported():
     assert _logprob() == rz.RZ_ENODEV
@@ -227,6 +272,8 @@ def test_no_device_is_reported():
     assert _is_loss() == rz.RZ_ENODEV
     assert rz.lib().rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_ENODEV
     assert _step() == rz.RZ_ENODEV
+    assert _shard() == rz.RZ_ENODEV
+    assert rz.lib().rz_logprob_merge(FAKE, FAKE, 10, 100, FAKE, FAKE, None) == rz.RZ_ENODEV
 
 
 def test_host_offset_validation():
