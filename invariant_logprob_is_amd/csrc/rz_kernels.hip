@@ -239,8 +239,9 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     float s = 0.0f;
-    const bool finite = Mj[j] != -INFINITY;
-    const float mb = tile_ref(Mj[j]);
+    // A column whose values are all -inf gets reference +inf: its exponents
+    // are -inf and its e exactly 0, with no select per value.
+    const float mb = Mj[j] != -INFINITY ? tile_ref(Mj[j]) : INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       u32x2 X[4];
@@ -249,7 +250,7 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
         float e[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          e[q] = finite ? __builtin_amdgcn_exp2f(fmaf(val(i, j, r4 * 4 + q), kLog2e, -mb)) : 0.0f;
+          e[q] = __builtin_amdgcn_exp2f(fmaf(val(i, j, r4 * 4 + q), kLog2e, -mb));
           s += e[q];
         }
         if (Store) {
