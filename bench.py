@@ -422,8 +422,13 @@ def main():
     }
     if not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_tokens} tokens ...")
-        out["cpu_baseline"] = cpu_baseline(b, args.cpu_tokens)
-        log(f"cpu baseline {out['cpu_baseline']['value']:.1f} tokens/s")
+        cb = cpu_baseline(b, args.cpu_tokens)
+        # the oracle's rate applied to the whole batch, and the GPU's rate over it
+        cb["full_batch_s_extrapolated"] = T / cb["value"]
+        cb["gpu_over_cpu"] = tokens_per_s / cb["value"]
+        out["cpu_baseline"] = cb
+        log(f"cpu baseline {cb['value']:.1f} tokens/s; full batch ~{cb['full_batch_s_extrapolated']:.0f} s; "
+            f"GPU/CPU {cb['gpu_over_cpu']:.0f}x")
     print(json.dumps(out), flush=True)
 
 
