@@ -361,17 +361,27 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
 // d_j = m - m_j (a bf16 exponent shift, 255 = flush), g = exp(m ln 2 - lse).
 // D[j * ds + t] holds d_j << 7 in both 16-bit halves.  lse is the float value
 // handed out, so the step and the stand-alone backward agree bit for bit.
-__device__ __forceinline__ void shift_tables(const float* __restrict__ pm, int64_t T, int64_t n_vt,
-                                             int64_t t, float m, float lse_f,
-                                             uint32_t* __restrict__ D, int64_t ds,
-                                             float* __restrict__ g) {
+__device__ __forceinline__ void shift_range(const float* __restrict__ pm, int64_t T, int64_t t,
+                                            int64_t j0, int64_t j1, float m,
+                                            uint32_t* __restrict__ D, int64_t ds) {
 #pragma unroll 8
-  for (int64_t j = 0; j < n_vt; ++j) {
+  for (int64_t j = j0; j < j1; ++j) {
     const float dm = m - tile_ref(pm[j * T + t]);
     const uint32_t d = (dm >= 0.0f && dm < 255.0f) ? uint32_t(dm) : 255u;
     D[j * ds + t] = (d << 7) | (d << 23);
   }
-  g[t] = float(exp(double(m) * kLn2 - double(lse_f)));
+}
+
+__device__ __forceinline__ float row_factor(float m, float lse_f) {
+  return float(exp(double(m) * kLn2 - double(lse_f)));
+}
+
+__device__ __forceinline__ void shift_tables(const float* __restrict__ pm, int64_t T, int64_t n_vt,
+                                             int64_t t, float m, float lse_f,
+                                             uint32_t* __restrict__ D, int64_t ds,
+                                             float* __restrict__ g) {
+  shift_range(pm, T, t, 0, n_vt, m, D, ds);
+  g[t] = row_factor(m, lse_f);
 }
 
 // max_j M_j (natural units) over the tiles of token t.
@@ -456,30 +466,41 @@ __device__ __forceinline__ double merge_splits(Part part, float& m_out) {
 // logprob = z_target - lse.  If cs is given (learner step), also
 // coef = cs * exp(logprob - mu), the same expression rz_is_loss evaluates,
 // and if D is given the shift table and row factor of the stored e.
-__global__ __launch_bounds__(256) void k_lse_combine(const float* __restrict__ pm,
-                                                     const float* __restrict__ ps,
-                                                     const float* __restrict__ ztgt, int64_t T,
-                                                     int64_t n_vt, float* __restrict__ logprob,
-                                                     float* __restrict__ lse,
-                                                     const double* __restrict__ cs,
-                                                     const float* __restrict__ mu,
-                                                     float* __restrict__ coef,
-                                                     uint32_t* __restrict__ D, int64_t ds,
-                                                     float* __restrict__ g) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= T) return;
-  SplitPart P[kVocabSplits];
-#pragma unroll
-  for (int q = 0; q < kVocabSplits; ++q)
-    P[q] = split_part(pm, ps, T, t, n_vt * q / kVocabSplits, n_vt * (q + 1) / kVocabSplits);
-  float m;
-  const double l = merge_splits([&](int q) -> const SplitPart& { return P[q]; }, m);
-  const float lp = float(double(ztgt[t]) - l);
-  const float lf = float(l);
-  logprob[t] = lp;
-  if (lse) lse[t] = lf;
-  if (cs) coef[t] = float(cs[t] * exp(double(lp) - double(mu[t])));
-  if (D) shift_tables(pm, T, n_vt, t, m, lf, D, ds, g);
+// A block covers 64 tokens with one wave per split: wave q reduces split q's
+// tiles for its lane's token (coalesced along tokens), wave 0 merges the 8
+// partials in split order, and each wave then writes its tiles' shifts.
+constexpr int kCombineThreads = 64 * kVocabSplits;
+
+__global__ __launch_bounds__(kCombineThreads) void k_lse_combine(
+    const float* __restrict__ pm, const float* __restrict__ ps, const float* __restrict__ ztgt,
+    int64_t T, int64_t n_vt, float* __restrict__ logprob, float* __restrict__ lse,
+    const double* __restrict__ cs, const float* __restrict__ mu, float* __restrict__ coef,
+    uint32_t* __restrict__ D, int64_t ds, float* __restrict__ g) {
+  __shared__ SplitPart part[kVocabSplits][64];
+  __shared__ float mref[64];
+  const int lane = threadIdx.x & 63;
+  const int q = threadIdx.x >> 6;
+  const int64_t t = int64_t(blockIdx.x) * 64 + lane;
+  const bool live = t < T;
+  const int64_t j0 = n_vt * q / kVocabSplits, j1 = n_vt * (q + 1) / kVocabSplits;
+  if (live) part[q][lane] = split_part(pm, ps, T, t, j0, j1);
+  __syncthreads();
+  if (q == 0 && live) {
+    float m;
+    const double l =
+        merge_splits([&](int s) -> const SplitPart& { return part[s][lane]; }, m);
+    const float lp = float(double(ztgt[t]) - l);
+    const float lf = float(l);
+    logprob[t] = lp;
+    if (lse) lse[t] = lf;
+    if (cs) coef[t] = float(cs[t] * exp(double(lp) - double(mu[t])));
+    if (D) g[t] = row_factor(m, lf);
+    mref[lane] = m;
+  }
+  if (D) {
+    __syncthreads();
+    if (live) shift_range(pm, T, t, j0, j1, mref[lane], D, ds);
+  }
 }
 
 // One row's record of one vocabulary split (struct rz_vocab_split).
@@ -1183,8 +1204,8 @@ hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztg
                               const float* mu, float* coef, uint32_t* D, int64_t ds, float* g,
                               hipStream_t s) {
   ProfScope prof("k_lse_combine", s);
-  hipLaunchKernelGGL(k_lse_combine, dim3(blocks_for(T, 256)), dim3(256), 0, s, pm, ps, ztgt, T,
-                     n_vocab_tiles(V), logprob, lse, cs, mu, coef, D, ds, g);
+  hipLaunchKernelGGL(k_lse_combine, dim3(blocks_for(T, 64)), dim3(kCombineThreads), 0, s, pm, ps,
+                     ztgt, T, n_vocab_tiles(V), logprob, lse, cs, mu, coef, D, ds, g);
   return hipGetLastError();
 }
 
