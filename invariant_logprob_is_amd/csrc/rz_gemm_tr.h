@@ -1,13 +1,15 @@
 // MFMA tile core for the token contraction of the LM-head weight gradient,
-//   C[v][h] = sum_t (e[t][v] 2^-d(t, vt)) hs[t][h],
-// with K = tokens.  Both operands are stored token-major (e in the
-// A-fragment order written by the forward, hs = coef g hhat as [T][H] rows),
-// so the MFMA fragments, which need 8 consecutive tokens per lane, are read
-// from LDS with gfx950's transposing read ds_read_b64_tr_b16: within each
-// group of 16 lanes, lane i receives element i % 4 of the 64-bit words that
-// lanes 4q + i / 4 (q = 0..3) address.  A source lane therefore addresses
-// 4 consecutive values (vocabulary or hidden) of one token; 16 lanes cover 4
-// tokens x 16 values and each lane receives 4 tokens of one value.
+//   C[v][h] = sum_t (e[t][v] 2^-d(t, vt)) hsT[h][t],
+// with K = tokens.  Operand B, hsT = (coef g hhat)^T, is token-contiguous and
+// staged exactly as in rz_gemm.h.  Operand A is e in the A-fragment order the
+// forward wrote for the P*W^T contraction (8 consecutive vocabulary values
+// of one token per lane), while this contraction needs 8 consecutive tokens
+// per lane: its fragments are read from LDS with gfx950's transposing read
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane i receives element
+// i % 4 of the 64-bit words that lanes 4q + i / 4 (q = 0..3) address.  A
+// source lane therefore addresses 4 consecutive vocabulary values of one
+// token; 16 lanes cover 4 tokens x 16 values and each lane receives 4 tokens
+// of one value.
 //
 // Tile 256 (vocabulary tile vt) x 256 (hidden tile ht), 4 waves of 128 x 128
 // as in rz_gemm.h, K stages of 64 tokens in a 2-stage LDS ring.  Per stage:
@@ -18,10 +20,9 @@
 //    transposing read touch 128 contiguous bytes; fragments of odd vocabulary
 //    steps also swap their 128-byte halves (slot L ^ 8), so the two 16-lane
 //    groups that the LDS serves together use different banks;
-//  - B: 64 token rows x 256 hidden of hs, as 4-token x 128-hidden pieces
-//    laid out [token/4][hidden half][token%4][16-byte chunk ^ 4 (token%4)]:
-//    each lane quad of a load reads 64 contiguous bytes of one row, and the
-//    XOR spreads a transposing read's 4 tokens over all banks;
+//  - B: 256 hidden rows x 64 tokens of hsT, 128 bytes per row with the
+//    16-byte chunks XOR-swizzled per row (rz_gemm.h's layout, read with
+//    plain 16-byte fragment reads);
 //  - the 64 per-token shifts d(t, vt) << 7 (256 bytes, wave 0 loads them).
 // The exponent shift is applied to the assembled A fragments with a
 // saturating packed 16-bit subtract, as in the P*W^T contraction.
@@ -54,11 +55,11 @@ struct GemmCoreTr {
   __amdgpu_buffer_rsrc_t ra, rb, rd;
   const char* e_tile0;    // e fragments of (token tile 0, vocabulary step vt*16)
   int64_t e_tile_stride;  // bytes between token tiles in the e block
-  uint32_t va[2], vb[8];  // per-lane load offsets (A within a fragment, even/odd step; B per piece)
+  uint32_t va[2], vb[8];  // per-lane load offsets (A within a fragment, even/odd step; B rows)
+  uint32_t boff;          // per-lane LDS offset of the B fragment reads (k-step 0)
   char* smem;
   int wave, nk, a_range, rot;
-  uint32_t rb_stage_bytes;  // 64 token rows of hs
-  uint32_t a_rd[4][2], b_rd[4][2];  // per-lane LDS byte offsets of the tr reads (k-step 0)
+  uint32_t a_rd[4][2];              // per-lane LDS byte offsets of the tr reads (k-step 0)
   uint32_t d_rd;                    // LDS offset of the lane's 8 token shifts (k-step 0)
   f32x16 acc[4][4];
   u32x4 fa[2][4], fb[2][4];  // fragments (8 bf16 each) as read
@@ -66,11 +67,11 @@ struct GemmCoreTr {
   u16x8 sh[2];            // per-set exponent shifts (d << 7) of the lane's 8 tokens
   u32x4 shr[2][2];        // the same as read from LDS (one token per 32-bit word)
 
-  // E: e block of the chunk (fragment order, n_ks = Vp/16 steps); hs: [TC][H]
-  // bf16 rows; D: shift table row of tile vt (d << 7 in the low 16 bits),
-  // at least TCp entries.
+  // E: e block of the chunk (fragment order, n_ks = Vp/16 steps); hsT: [H][TCp]
+  // bf16 rows (zero for tokens past the chunk); D: shift table row of tile vt
+  // (d << 7 in the low 16 bits), at least TCp entries.
   __device__ __forceinline__ void init(const uint16_t* E, int64_t n_ks, int64_t vt,
-                                       const uint16_t* hs, int64_t TC, int H, int64_t ht,
+                                       const uint16_t* hsT, int H, int64_t ht,
                                        const uint32_t* Drow, int64_t TCp, char* lds) {
     smem = lds;
     lds_base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
@@ -87,14 +88,7 @@ struct GemmCoreTr {
     const int64_t left = n_ks - vt * 16;
     a_range = int(left < 16 ? left : 16) * 8 * 1024;
     set_a_tile(0);
-    {
-      const uint64_t p = reinterpret_cast<uint64_t>(hs + ht * kTile);
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(p >> 32));
-      const int n = __builtin_amdgcn_readfirstlane(int(TC * H * 2 - ht * kTile * 2));
-      rb = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uint64_t(hi) << 32) | lo), 0,
-                                             n, kBufferFlags);
-    }
+    rb = tile_rsrc(hsT, ht * kTile, H, TCp);
     {
       const uint64_t p = reinterpret_cast<uint64_t>(Drow);
       const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(p));
@@ -110,13 +104,16 @@ struct GemmCoreTr {
       const int L = lane ^ (8 * o);
       va[o] = uint32_t(((L >> 3) << 2) + (L & 3) + 32 * ((L >> 2) & 1)) * 16u;
     }
-    // B piece q = wave*8 + u: token 4*(q/2) + lane/16, hidden half q%2, LDS
-    // chunk lane%16 <- row chunk (lane%16) ^ 4*(lane/16)
+    // B load q = wave*8 + u: rows 8q .. 8q+7, lane -> row 8q + lane/8, LDS
+    // slot lane%8 holding the row's chunk (lane%8) ^ swz(row)
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int q = wave * 8 + u;
-      const int tq = lane >> 4;
-      vb[u] = uint32_t((4 * (q >> 1) + tq) * H * 2 + (q & 1) * 256 + ((lane & 15) ^ (4 * tq)) * 16);
+      const uint32_t row = uint32_t((wave * 8 + u) * 8 + lane / 8);
+      vb[u] = row * uint32_t(TCp) * 2u + ((uint32_t(lane % 8) ^ swz(row)) * 16u);
+    }
+    {
+      const uint32_t r32 = uint32_t(lane & 31);
+      boff = uint32_t(kA) + uint32_t(wn * 128 + r32) * 128u + ((uint32_t(lane >> 5) ^ swz(r32)) << 4);
     }
     // tr-read addresses for k-step 0 (read_step adds the k-step's offsets)
     const int g = lane >> 4, s = lane & 15, q = s >> 2, j = s & 3;
@@ -130,10 +127,6 @@ struct GemmCoreTr {
         const int t = 8 * (g >> 1) + 4 * h + q;
         const int slot = ((t >> 2) * 8 + (j >> 1) * 4 + (t & 3)) ^ (8 * (ksl & 1));
         a_rd[i][h] = uint32_t(ksl * 2 * 1024 + slot * 16 + 8 * (j & 1));
-        // B block i of wave wn: hidden half wn, chunk 4i + 2(g%2) + j/2
-        const int c = 4 * i + 2 * (g & 1) + (j >> 1);
-        b_rd[i][h] = uint32_t(kA + ((t >> 2) * 2 + wn) * 1024 + (t & 3) * 256 +
-                              (c ^ (4 * (t & 3))) * 16 + 8 * (j & 1));
       }
     // the lane's 8 token shifts: tokens 8*(lane/32) .. +7 of the k-step
     d_rd = uint32_t(kA + kB + (lane >> 5) * 8 * 4);
@@ -167,9 +160,8 @@ struct GemmCoreTr {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
                                              uint32_t((q >> 1) * 8192 + (q & 1) * 1024) + va[(u >> 1) & 1],
                                              soffA, 0, 0);
-    // the whole offset in voffset: rows past TC must fail the range check
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16,
-                                             vb[u] + uint32_t(st) * rb_stage_bytes, 0, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16, vb[u],
+                                             st * 128, 0, 0);
     if (u == 0 && wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(s + kA + kB), 4,
                                                uint32_t((threadIdx.x & 63) * 4), st * 256, 0, 0);
@@ -179,22 +171,20 @@ struct GemmCoreTr {
     // (the next 1 KB fragment), rows (kk%2)*16 of it (4 slot groups of 8)
     return uint32_t((kk >> 1) * 1024 + (kk & 1) * 4 * 8 * 16);
   }
-  static __device__ __forceinline__ uint32_t db_of(int kk) { return uint32_t(kk * 4 * 2 * 1024); }
 
-  // Read unit u (0..7) of k-step kk into set F: A block u (u < 4) or B block
-  // u - 4, two transposing reads each.
+  // Read unit u (0..7) of k-step kk into set F: A block u (u < 4, two
+  // transposing reads) or B block u - 4 (one 16-byte read).
   template <int F>
   __device__ __forceinline__ void read_unit(const char* s, int kk, int u) {
-    const uint32_t b = lds_base + uint32_t(s - smem);
-    const uint32_t* rd = u < 4 ? a_rd[u] : b_rd[u - 4];
-    const uint32_t o = u < 4 ? da_of(kk) : db_of(kk);
-    const u32x2 lo = ds_read_tr16(b + rd[0] + o);
-    const u32x2 hi = ds_read_tr16(b + rd[1] + o);
-    const u32x4 v = {lo[0], lo[1], hi[0], hi[1]};
-    if (u < 4)
-      fa[F][u] = v;
-    else
-      fb[F][u - 4] = v;
+    if (u < 4) {
+      const uint32_t b = lds_base + uint32_t(s - smem) + da_of(kk);
+      const u32x2 lo = ds_read_tr16(b + a_rd[u][0]);
+      const u32x2 hi = ds_read_tr16(b + a_rd[u][1]);
+      fa[F][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    } else {
+      fb[F][u - 4] =
+          *reinterpret_cast<const u32x4*>(s + (boff ^ uint32_t(kk << 5)) + (u - 4) * 32 * 128);
+    }
   }
 
   // Wait for every LDS read in flight, with the set-F fragments as operands
@@ -306,8 +296,7 @@ struct GemmCoreTr {
 
   // K = TCp tokens (a multiple of 256).  Ends with no load in flight and no
   // LDS read outstanding.
-  __device__ __forceinline__ void run(int K, int H) {
-    rb_stage_bytes = uint32_t(64 * H * 2);
+  __device__ __forceinline__ void run(int K) {
     nk = K / 64;
 #pragma unroll
     for (int u = 0; u < 8; ++u) load_pair(0, u);

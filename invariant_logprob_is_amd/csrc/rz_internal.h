@@ -96,8 +96,8 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.s_coef = o; o = align256(o + size_t(T) * 4);
   L.s_part = o; o = align256(o + size_t(T + 8) * 8);
   L.step_end = o;
-  // the chunk's hhat rows scaled by coef_t g_t (bf16)
-  L.g_hs = o;   o = align256(o + size_t(tc) * H * 2);
+  // the chunk's hhat rows scaled by coef_t g_t (bf16), token-contiguous
+  L.g_hs = o;   o = align256(o + size_t(H) * tcp * 2);
   // count, cursor, offsets, bucket slots, sorted order, scan block totals;
   // then the chunk's row factors r_t (float64)
   L.g_ibuf = o; o = align256(o + align256(size_t(3 * V + 1 + 2 * tc + ceil_div(V, 1024) + 1) * 4)

@@ -909,32 +909,39 @@ __global__ __launch_bounds__(256) void k_decompose_final(const double* __restric
 // after a deterministic bucketing of the chunk's tokens by target.
 // ---------------------------------------------------------------------------
 
-// hs[t][h] = bf16(coef_t g_t hhat[t][h]) for the chunk's tokens (the
-// per-token factor of p moved onto the other operand of the token
-// contraction; one rounding).  One wave per row, 8 values per lane step.
-__global__ __launch_bounds__(256) void k_scale_rows(const uint16_t* __restrict__ hh,
-                                                    const float* __restrict__ coef,
-                                                    const float* __restrict__ gf, int64_t TC, int H,
-                                                    uint16_t* __restrict__ hs) {
-  const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
-  if (t >= TC) return;
-  const int lane = threadIdx.x & 63;
-  const float sc = coef[t] * gf[t];
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(hh + t * H + c);
-    u32x4 o;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      o[q] = pack_bf16x2(__uint_as_float(v[q] << 16) * sc, __uint_as_float(v[q] & 0xFFFF0000u) * sc);
-    *reinterpret_cast<u32x4*>(hs + t * H + c) = o;
+// hsT[h][t] = bf16(coef_t g_t hhat[t][h]) for the chunk's tokens t < TC
+// and 0 for TC <= t < TCp (the per-token factor of p moved onto the other
+// operand of the token contraction; one rounding), token-contiguous so that
+// the contraction reads it as a plain row-major operand.  64 x 64 tiles
+// through LDS.
+__global__ __launch_bounds__(256) void k_scale_rows_t(const uint16_t* __restrict__ hh,
+                                                      const float* __restrict__ coef,
+                                                      const float* __restrict__ gf, int64_t TC,
+                                                      int64_t TCp, int H,
+                                                      uint16_t* __restrict__ hsT) {
+  __shared__ uint16_t tile[64][66];
+  const int64_t t0 = int64_t(blockIdx.x) * 64;
+  const int h0 = blockIdx.y * 64;
+  const int tx = threadIdx.x & 63;
+  const int ty = threadIdx.x >> 6;
+  for (int r = ty; r < 64; r += 4) {
+    const int64_t t = t0 + r;
+    uint16_t v = 0;
+    if (t < TC) {
+      const float x = __uint_as_float(uint32_t(hh[t * H + h0 + tx]) << 16);
+      v = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x * (coef[t] * gf[t])));
+    }
+    tile[r][tx] = v;
   }
+  __syncthreads();
+  for (int r = ty; r < 64; r += 4) hsT[int64_t(h0 + r) * TCp + t0 + tx] = tile[tx][r];
 }
 
 // The softmax part of dW straight from the stored e (GemmCoreTr): dW[v][h] =
-// (first ? 0 : dW[v][h]) - sum_t (e_tv 2^-d(t, vt)) hs[t][h].
+// (first ? 0 : dW[v][h]) - sum_t (e_tv 2^-d(t, vt)) hsT[h][t].
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
-             const uint16_t* __restrict__ hs, int64_t TC, int64_t TCp, int H, int V, int64_t Vp,
+             const uint16_t* __restrict__ hsT, int64_t TCp, int H, int V, int64_t Vp,
              int64_t n_vt, int64_t n_ht, int first, float* __restrict__ dW) {
   __shared__ __attribute__((aligned(16))) char lds[GemmCoreTr::kRing];
   int64_t vt, ht;
@@ -942,8 +949,8 @@ void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int
   const int64_t v0 = vt * kTile;
   const int64_t h0 = ht * kTile;
   GemmCoreTr g;
-  g.init(E, Vp / 16, vt, hs, TC, H, ht, D + vt * ds, TCp, lds);
-  g.run(int(TCp), H);
+  g.init(E, Vp / 16, vt, hsT, H, ht, D + vt * ds, TCp, lds);
+  g.run(int(TCp));
   f32x16 (&acc)[4][4] = g.acc;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -1298,15 +1305,15 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                        s, dhh_chunk, x_chunk, rbuf, TC, H, gb0, gpart);
   }
   {
-    // hs = coef g hhat (the chunk's rows), then the token contraction
-    // straight from the stored e
+    // hsT = coef g hhat (the chunk's rows, token-contiguous), then the token
+    // contraction straight from the stored e
     ProfScope prof("k_dw", s);
-    hipLaunchKernelGGL(k_scale_rows, dim3(blocks_for(TC, 4)), dim3(256), 0, s, hh, coef_chunk, g,
-                       TC, H, hs);
+    hipLaunchKernelGGL(k_scale_rows_t, dim3(uint32_t(TCp / 64), H / 64), dim3(256), 0, s, hh,
+                       coef_chunk, g, TC, TCp, H, hs);
     const int64_t n_vt = n_vocab_tiles(V);
     const int64_t n_ht = ceil_div(H, kTile);
     hipLaunchKernelGGL(k_dw_tr, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, E, D, ds,
-                       hs, TC, TCp, H, V, Vp, n_vt, n_ht, first, dW);
+                       hs, TCp, H, V, Vp, n_vt, n_ht, first, dW);
   }
   {
     ProfScope prof("k_onehot", s);
