@@ -116,7 +116,7 @@ def summarize_counters(fetch_csv: str, write_csv: str):
     # the learner step launches the storing forward variant; k_dw (--grads)
     # is the row scaling plus the token contraction, one of each per chunk
     for k, disps in (("k_lmhead_fwd", ("k_lmhead_fwd<true>",)), ("k_dhidden", ("k_dhidden",)),
-                     ("k_dw", ("k_scale_rows", "k_dw_tr"))):
+                     ("k_dw", ("k_scale_rows_t", "k_dw_tr"))):
         if any(d not in fetch or d not in write for d in disps):
             continue
         disp = disps[-1]
