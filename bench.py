@@ -208,6 +208,25 @@ def probe(args, b, rz, x, g, W, tgt, lp, ws, stream):
     }), flush=True)
 
 
+def executed_flops(T: int, H: int, V: int, grads: bool) -> float:
+    """MFMA flops the step's kernels execute, from their tile grids: the
+    stored e replaces a second forward, so the only work beyond the
+    algorithmic count is the padding of the edge tiles (256-row tiles of
+    tokens per 32768-token chunk, of V and of H; V padded to 64 along K)."""
+    def up(a, b):
+        return -(-a // b) * b
+    chunks = [min(32768, T - c) for c in range(0, T, 32768)]
+    Vt, Ht, Vk = up(V, 256), up(H, 256), up(V, 64)
+    f = 0.0
+    for tc in chunks:
+        tp = up(tc, 256)
+        f += 2.0 * Vt * tp * H          # forward: vocab x token tiles, K = H
+        f += 2.0 * tp * Ht * Vk         # hidden-state contraction, K = V padded to 64
+        if grads:
+            f += 2.0 * Vt * Ht * tp     # dW: vocab x hidden tiles, K = tokens
+    return f
+
+
 def shards(args, b, rz, x, g, W, tgt, lp, lse, ws):
     """The log-probabilities of the workload through `args.shards` equal
     shares of the vocabulary splits (rz_logprob_shard on each share's rows of
@@ -392,6 +411,7 @@ def main():
     T, H, V = b.T, b.H, b.V
     tokens_per_s = T / (ms_step / 1000.0)
     alg_flops_token = (6.0 if args.grads else 4.0) * H * V
+    exec_flops_token = executed_flops(T, H, V, args.grads) / T
     gemm_flops_step = 2.0 * T * H * V      # algorithmic flops of each GEMM kernel per step
     kernels = {}
     for k in ("k_lmhead_fwd", "k_dhidden") + (("k_dw",) if args.grads else ()):
@@ -417,6 +437,8 @@ def main():
         "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}, {b.R} responses in {b.G} groups",
                    "T": T, "H": H, "V": V, "R": b.R, "G": b.G},
         "mfma_frac_algorithmic": tokens_per_s * alg_flops_token / PEAK_BF16_FLOPS,
+        "executed_flops_per_token": exec_flops_token,
+        "mfma_frac_executed": tokens_per_s * exec_flops_token / PEAK_BF16_FLOPS,
         "kernels": kernels,
         "roofline": roofline,
     }
