@@ -58,7 +58,7 @@ struct GemmCoreTr {
   uint32_t va[2], vb[8];  // per-lane load offsets (A within a fragment, even/odd step; B rows)
   uint32_t boff;          // per-lane LDS offset of the B fragment reads (k-step 0)
   char* smem;
-  int wave, nk, a_range, rot;
+  int wave, nk, a_range;
   uint32_t a_rd[4][2];              // per-lane LDS byte offsets of the tr reads (k-step 0)
   uint32_t d_rd;                    // LDS offset of the lane's 8 token shifts (k-step 0)
   f32x16 acc[4][4];
@@ -81,7 +81,6 @@ struct GemmCoreTr {
     const int wn = wave >> 1;
     e_tile0 = reinterpret_cast<const char*>(E) + frag_offset(0, vt * 16, 0, n_ks);
     e_tile_stride = n_ks * 8 * 1024;
-    rot = __builtin_amdgcn_readfirstlane(int(vt & 3));
     // the last vocabulary tile may hold fewer than 16 steps (the vocabulary is
     // padded to 64): its missing fragments read as 0 instead of running into
     // the next token tile or past the block
@@ -141,30 +140,21 @@ struct GemmCoreTr {
                                            __builtin_amdgcn_readfirstlane(a_range), kBufferFlags);
   }
 
-  // Token stage (64 tokens) that stage kt covers: the 4 stages of a token
-  // tile are taken in an order rotated by the vocabulary tile, so that
-  // workgroups running side by side read different 2 KB pieces of their e
-  // blocks at the same time (the pieces of one stage lie 8 KB apart).
-  __device__ __forceinline__ int stage_tokens(int kt) const {
-    return (kt & ~3) | (((kt & 3) + rot) & 3);
-  }
-
   // Loads of stage kt: pair u (0..7) = A fragment and B piece q = wave*8 + u;
   // wave 0 also loads the stage's shifts with pair 0.
   __device__ __forceinline__ void load_pair(int kt, int u) {
     char* s = smem + (kt & 1) * kStage;
     const int q = wave * 8 + u;
-    const int st = stage_tokens(kt);
-    // A fragment q: vocabulary step q/2, token block 2*(st%4) + q%2 of the tile
-    const int soffA = ((st & 3) * 2) * 1024;
+    // A fragment q: vocabulary step q/2, token block 2*(kt%4) + q%2 of the tile
+    const int soffA = ((kt & 3) * 2) * 1024;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
                                              uint32_t((q >> 1) * 8192 + (q & 1) * 1024) + va[(u >> 1) & 1],
                                              soffA, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16, vb[u],
-                                             st * 128, 0, 0);
+                                             kt * 128, 0, 0);
     if (u == 0 && wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(s + kA + kB), 4,
-                                               uint32_t((threadIdx.x & 63) * 4), st * 256, 0, 0);
+                                               uint32_t((threadIdx.x & 63) * 4), kt * 256, 0, 0);
   }
   static __device__ __forceinline__ uint32_t da_of(int kk) {
     // k-step kk = tokens 16kk .. 16kk+15 of the stage: token block kk/2
