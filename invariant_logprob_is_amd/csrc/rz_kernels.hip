@@ -170,8 +170,9 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 //      from M with the same float expression wherever it is needed.
 // Every token goes through the same operations whatever its column or tile
 // position, so the partial (M, S) of a token depends only on that token's
-// row.  Partials are written per vocabulary tile and merged in tile order by
-// k_lse_combine.  With Store, the values e (rounded to bf16) are also written
+// row.  Partials are written per vocabulary tile and merged by k_lse_combine
+// in its fixed two-level order (tiles within each vocabulary split, then the
+// splits).  With Store, the values e (rounded to bf16) are also written
 // out, straight from registers, in the fragment order of the contraction that
 // consumes them (frag_offset, token tiles x 16-wide vocabulary steps):
 // lanes l and l+32 of a 32x32 block hold vocabulary rows 8q..8q+3 and
