@@ -38,10 +38,17 @@ def log(msg):
 
 
 def source_sha() -> str:
+    """Hash of the kernel sources' code: comments and blank lines are left
+    out, so a documentation edit does not invalidate measured counters."""
+    import re
     h = hashlib.sha256()
     for p in KERNEL_SOURCES:
-        with open(p, "rb") as f:
-            h.update(f.read())
+        with open(p, encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        lines = [ln.rstrip() for ln in src.splitlines()]
+        h.update("\n".join(ln for ln in lines if ln).encode())
     return h.hexdigest()[:16]
 
 
