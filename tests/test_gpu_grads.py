@@ -19,6 +19,12 @@ from gpu_util import bf16, bits32, f32, host, i32, rel_fro, say
 pytestmark = pytest.mark.gpu
 
 DW_RTOL = 1e-3
+# Rows whose softmax is dominated by one or two entries (logit std of several
+# nats): dW[v] is then a sum of few terms, each carrying the bf16 rounding of
+# e (stored by the forward) and of coef g hhat (the contraction's B operand),
+# unit roundoff 2^-9 each, so its relative error is of order 2^-9 sqrt 2 =
+# 2.8e-3 and does not average out.
+DW_WIDE_RTOL = 5e-3
 
 
 @pytest.fixture(scope="module")
@@ -56,12 +62,19 @@ def _oracle_grads(x, g, W, t, mu, ro, go, reward):
     return oracle.weight_grads(x, g, 1e-6, W, t, olse, coef)
 
 
-@pytest.mark.parametrize("T,H,V,same", [(300, 128, 1024, False), (257, 192, 513, False),
-                                        (1, 64, 65, False), (40000, 128, 1000, False),
-                                        (600, 64, 300, True)])
-def test_weight_grads_match_oracle(rz, gpu, T, H, V, same):
-    say(f"weight grads T={T} H={H} V={V} same_target={same}")
-    x, g, W, t, mu = _case(T + H + V, T, H, V, same)
+@pytest.mark.parametrize("T,H,V,same,zstd", [(300, 128, 1024, False, None), (257, 192, 513, False, None),
+                                             (1, 64, 65, False, None), (40000, 128, 1000, False, None),
+                                             (600, 64, 300, True, None),
+                                             # the largest hidden size: 64 hidden tiles, the
+                                             # grouped tile raster of the token contraction
+                                             (200, 16384, 700, False, 0.8),
+                                             # peaked rows (see DW_WIDE_RTOL)
+                                             (300, 128, 3000, False, 5.7),
+                                             (200, 16384, 700, False, 6.4)])
+def test_weight_grads_match_oracle(rz, gpu, T, H, V, same, zstd):
+    say(f"weight grads T={T} H={H} V={V} same_target={same} logit std={zstd}")
+    wstd = 0.05 if zstd is None else zstd / math.sqrt(H)
+    x, g, W, t, mu = _case(T + H + V, T, H, V, same, wstd)
     ro, go, reward = _ragged(T, T, 1, 1) if T == 1 else _ragged(T, T, 2, 2) if T < 8 else \
         _ragged(T, T, 4, 4)
     d = [bf16(a, gpu) for a in (x, g, W)]
@@ -75,7 +88,8 @@ def test_weight_grads_match_oracle(rz, gpu, T, H, V, same):
     e_w = rel_fro(host(out["dW"]), odW)
     e_g = float(np.linalg.norm(host(out["dgamma"]) - odg) / np.linalg.norm(odg))
     say(f"  dW rel_fro={e_w:.2e} dgamma rel={e_g:.2e}")
-    assert e_w <= DW_RTOL and e_g <= DW_RTOL
+    tol = DW_WIDE_RTOL if (zstd or 0) > 2 else DW_RTOL
+    assert e_w <= tol and e_g <= tol
 
 
 def test_weight_grads_leave_other_outputs_unchanged_and_are_deterministic(rz, gpu):
