@@ -68,3 +68,29 @@ def test_largest_vocabulary(rz, gpu):
                                           row_chunk=8))
     say(f"  max|dlogprob|={np.abs(host(lp) - olp).max():.2e} dhidden rel_fro={e:.2e}")
     assert e <= DH_RTOL
+
+
+def test_largest_vocabulary_weight_grads(rz, gpu):
+    # the learner step with dW and dgamma at V = 4,000,000: 15625 vocabulary
+    # tiles in the token contraction and a one-hot bucketing over 4M rows
+    T, H, V = 16, 64, 4_000_000
+    say(f"limits weight grads V={V}")
+    x, g, W, t = _case(5, T, H, V, 0.05)
+    t[:4] = [0, V - 1, V - 256, V // 2]
+    t[4] = t[5] = 1234567                           # two tokens on one target row
+    ro = np.array([0, 4, 8, 12, 16], np.int64)
+    go = np.array([0, 2, 4], np.int64)
+    reward = np.array([1.0, 0.0, 0.0, 1.0], np.float32)
+    say("  oracle logprob")
+    olp, olse = oracle.logprob(x, g, 1e-6, W, t, row_chunk=8)
+    mu = (olp + np.random.default_rng(6).normal(0, 0.05, T)).astype(np.float32)
+    d = [bf16(a, gpu) for a in (x, g, W)]
+    out = rz.learner_step(d[0], d[1], d[2], i32(t, gpu), f32(mu, gpu), ro, go, reward,
+                          weight_grads=True)
+    say("  oracle weight grads")
+    coef = oracle.is_loss(olp, mu.astype(np.float64), ro, go, reward)["coef"]
+    odW, odg = oracle.weight_grads(x, g, 1e-6, W, t, olse, coef)
+    e_w = rel_fro(host(out["dW"]), odW)
+    e_g = float(np.linalg.norm(host(out["dgamma"]) - odg) / np.linalg.norm(odg))
+    say(f"  dW rel_fro={e_w:.2e} dgamma rel={e_g:.2e}")
+    assert e_w <= DH_RTOL and e_g <= DH_RTOL
