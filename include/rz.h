@@ -41,8 +41,9 @@
  *     that target (the caller applies the next-token shift and drops prompt
  *     tokens).  Tokens of a response are contiguous; the responses of one
  *     prompt group are contiguous.
- *   - Thread safety: no global mutable state; concurrent calls are safe if
- *     they use distinct workspaces and outputs.
+ *   - Thread safety: no global mutable state apart from the opt-in timing
+ *     records of rz_profile_* (process-wide, behind a lock); concurrent
+ *     calls are safe if they use distinct workspaces and outputs.
  */
 #ifndef RZ_H_
 #define RZ_H_
