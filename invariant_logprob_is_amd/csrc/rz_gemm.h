@@ -66,14 +66,14 @@ __device__ __forceinline__ uint32_t swz(uint32_t row) {
 }
 
 // Output coordinates of acc[i][j][r] inside the workgroup tile, for lane l of
-// wave (wm, wn):
+// wave (wm, wn) owning nb B blocks (4 with 4 waves, 2 with 8):
 //   a = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4      (operand-A row)
-//   b = wn*128 + j*32 + l%32                          (operand-B row)
+//   b = wn*32*nb + j*32 + l%32                        (operand-B row)
 __device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
   return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
-__device__ __forceinline__ int acc_col(int wn, int j, int lane) {
-  return wn * 128 + j * 32 + (lane & 31);
+__device__ __forceinline__ int acc_col(int wn, int j, int lane, int nb = 4) {
+  return wn * 32 * nb + j * 32 + (lane & 31);
 }
 
 __device__ __forceinline__ void zero_acc(f32x16 (&acc)[4][4]) {
@@ -130,16 +130,27 @@ __host__ __device__ constexpr int64_t frag_offset(int64_t tile, int64_t ks, int6
   return ((tile * n_ks + ks) * 8 + mb) * 1024;  // bytes
 }
 
-template <bool ShiftA, bool ANative = false>
+// NW: waves per workgroup, 4 (one per SIMD, each owning 128 x 128 of the
+// tile: 4 x 4 blocks) or 8 (two per SIMD, each owning 128 x 64: 4 x 2
+// blocks, accumulators small enough for two waves' registers, so one wave's
+// MFMAs issue while the other waits on LDS, loads or the barrier).  Waves
+// form a 2 x NW/2 grid: wm picks the 128 A rows, wn the 256/(NW/2) B rows.
+template <bool ShiftA, bool ANative = false, int NW = 4>
 struct GemmCoreT {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static constexpr int kNB = 16 / NW;                        // B blocks per wave
+  static constexpr int kLP = kTile / kRowsPerLoad / NW;      // loads per wave per operand
+  static constexpr int kNM = 4 * kNB;                        // MFMAs per step
+  static constexpr int kNR = 4 + kNB;                        // fragment reads per step
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[kLoadsPerOp];  // per-lane byte offsets of the load instructions (B, and A if row-major)
+  uint32_t va[8];            // per-lane byte offsets of the load instructions (B, and A if
+                             // row-major); the first kLP are used
   uint32_t aoff, boff;       // per-lane LDS byte offsets of fragment reads (step 0)
   char* smem;
   int wave;
   int nk;                    // number of stages (K / kBK)
-  f32x16 acc[4][4];
-  bf16x8 fa[2][4], fb[2][4];
+  f32x16 acc[4][kNB];
+  bf16x8 fa[2][4], fb[2][kNB];
   // ShiftA only: per-lane table pointer (row of block 0), current and next
   // K block's shifts of the lane's four fragment rows.
   const uint32_t* dsrc;
@@ -179,12 +190,12 @@ struct GemmCoreT {
       ra = tile_rsrc(A, a0, a_rows, ld);
     }
     rb = tile_rsrc(B, b0, b_rows, ld);
-    // Load instruction q = wave*kLoadsPerOp + j moves rows [q*R, q*R + R)
+    // Load instruction q = wave*kLP + j moves rows [q*R, q*R + R)
     // (R = kRowsPerLoad); lane -> row q*R + lane/kChunks and LDS slot
     // lane%kChunks, which holds global chunk slot ^ swz(row).
 #pragma unroll
-    for (int j = 0; j < kLoadsPerOp; ++j) {
-      const uint32_t row = uint32_t((wave * kLoadsPerOp + j) * kRowsPerLoad + lane / kChunks);
+    for (int j = 0; j < kLP; ++j) {
+      const uint32_t row = uint32_t((wave * kLP + j) * kRowsPerLoad + lane / kChunks);
       const uint32_t chunk = uint32_t(lane % kChunks) ^ swz(row);
       va[j] = row * uint32_t(ld) * 2u + chunk * 16u;
     }
@@ -193,15 +204,20 @@ struct GemmCoreT {
     const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
     aoff = ANative ? uint32_t(wm * 4 * 1024 + lane * 16)
                    : uint32_t(wm * 128 + r32) * kRowBytes + slot0;
-    boff = uint32_t(kOpStageBytes) + uint32_t(wn * 128 + r32) * kRowBytes + slot0;
-    zero_acc(acc);
+    boff = uint32_t(kOpStageBytes) + uint32_t(wn * 32 * kNB + r32) * kRowBytes + slot0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
   // Load pair j (one A and one B instruction) of stage kt.
   __device__ __forceinline__ void load_pair(int kt, int j) {
     const int soff = kt * kRowBytes;
     char* s = smem + (kt % kStages) * kStageBytes;
-    const int q = wave * kLoadsPerOp + j;
+    const int q = wave * kLP + j;
     if (ANative)  // piece q of the stage's contiguous 32 KB block, lane-major as stored
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
                                                uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
@@ -213,7 +229,7 @@ struct GemmCoreT {
                                              va[j], soff, 0, 0);
   }
 
-  // Fragment read number q (0..7) into set F: A blocks first.
+  // Fragment read number q (0 .. kNR-1) into set F: A blocks first.
   template <int F>
   __device__ __forceinline__ void read_one(const char* s, uint32_t oa, uint32_t ob, int q) {
     constexpr int kBlockBytes = 32 * kRowBytes;
@@ -226,7 +242,7 @@ struct GemmCoreT {
 
   template <int F>
   __device__ __forceinline__ void mfma_one(int idx) {
-    const int i = idx >> 2, j = idx & 3;
+    const int i = idx / kNB, j = idx % kNB;
     acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
   }
 
@@ -278,12 +294,12 @@ struct GemmCoreT {
     const uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
     const uint32_t ob = boff ^ uint32_t(kk << 5);
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
+    for (int idx = 0; idx < kNM; ++idx) {
       mfma_one<F>(idx);
-      if (idx < 8) read_one<F ^ 1>(s, oa, ob, idx);
-      if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLoadsPerOp)
+      if (idx < kNR) read_one<F ^ 1>(s, oa, ob, idx);
+      if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLP)
         load_pair(lkt, first_pair + (idx >> 2));
-      if ((idx & 3) == 3 && idx < 15) shift_frag<F>((idx >> 2) + 1);
+      if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<F>(idx / kNB + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     shift_frag<F ^ 1>(0);
@@ -304,14 +320,15 @@ struct GemmCoreT {
     // steps 0 .. kSteps-2 (sets alternate 0,1,0,...), each reading the next step
     step<0, Load>(s, 1, lkt, 0);
     if (kSteps == 4) {
-      step<1, Load>(s, 2, lkt, 4);
-      step<0, false>(s, 3, lkt, 8);
+      step<1, Load>(s, 2, lkt, kNM / 4);
+      step<0, false>(s, 3, lkt, 0);
     }
-    // last step (set 1): eight MFMAs, publish stage kt+1, eight MFMAs with its reads
+    // last step (set 1): half its MFMAs, publish stage kt+1, the other half
+    // with the reads of its step 0
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) {
+    for (int idx = 0; idx < kNM / 2; ++idx) {
       mfma_one<1>(idx);
-      if ((idx & 3) == 3) shift_frag<1>((idx >> 2) + 1);
+      if (idx % kNB == kNB - 1) shift_frag<1>(idx / kNB + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (More) {
@@ -319,10 +336,13 @@ struct GemmCoreT {
       barrier();
       const char* sn = smem + ((kt + 1) % kStages) * kStageBytes;
 #pragma unroll
-      for (int idx = 8; idx < 16; ++idx) {
+      for (int idx = kNM / 2; idx < kNM; ++idx) {
         mfma_one<1>(idx);
-        read_one<0>(sn, aoff, boff, idx - 8);
-        if (idx == 11) shift_frag<1>(3);
+        // read u goes with MFMA kNM/2 + u (kNM/2) / kNR: one or two per MFMA
+#pragma unroll
+        for (int u = 0; u < kNR; ++u)
+          if (u * (kNM / 2) / kNR == idx - kNM / 2) read_one<0>(sn, aoff, boff, u);
+        if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<1>(idx / kNB + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ShiftA) {
@@ -334,9 +354,9 @@ struct GemmCoreT {
       __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
-      for (int idx = 8; idx < 16; ++idx) {
+      for (int idx = kNM / 2; idx < kNM; ++idx) {
         mfma_one<1>(idx);
-        if (idx == 11) shift_frag<1>(3);
+        if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<1>(idx / kNB + 1);
       }
     }
   }
@@ -348,12 +368,12 @@ struct GemmCoreT {
     const int pre = nk < kStages - 1 ? nk : kStages - 1;
     for (int st = 0; st < pre; ++st)
 #pragma unroll
-      for (int j = 0; j < kLoadsPerOp; ++j) load_pair(st, j);
+      for (int j = 0; j < kLP; ++j) load_pair(st, j);
     if (ShiftA) load_shift(0, dsh);
     wait_loads_except(pre - 1);
     barrier();
 #pragma unroll
-    for (int q = 0; q < 8; ++q) read_one<0>(smem, aoff, boff, q);
+    for (int q = 0; q < kNR; ++q) read_one<0>(smem, aoff, boff, q);
     shift_frag<0>(0);
     int kt = 0;
     for (; kt + kStages - 1 < nk; ++kt) stage<true, true>(kt);

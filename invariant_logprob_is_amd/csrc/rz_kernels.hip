@@ -190,8 +190,8 @@ constexpr int kFwdLds = kLdsBytes + 2048;  // the GEMM ring + the exchange area
 // -inf.  The masked values are formed on the fly instead of written into
 // the accumulators: in-place writes there make the compiler spill in every
 // tile's epilogue.
-template <bool Store, bool Mask>
-__device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* lds, int64_t tt,
+template <bool Store, bool Mask, int NB>
+__device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* lds, int64_t tt,
                                              int64_t vt, int64_t T, int V, int64_t Vp,
                                              float* __restrict__ pm, float* __restrict__ ps,
                                              uint16_t* __restrict__ E) {
@@ -211,9 +211,9 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
   };
 
   // 1. tile max
-  float Mj[4];
+  float Mj[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NB; ++j) {
     float m = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -223,22 +223,22 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
   }
   if (half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xch[(wm * 8 + wn * 4 + j) * 32 + col] = Mj[j];
+    for (int j = 0; j < NB; ++j) xch[(wm * 8 + wn * NB + j) * 32 + col] = Mj[j];
   }
   // The exchanges below order LDS traffic only: a bare barrier, so the
   // e stores already issued keep draining instead of being waited for.
   GemmCore::barrier();
 #pragma unroll
-  for (int j = 0; j < 4; ++j) Mj[j] = fmaxf(Mj[j], xch[((wm ^ 1) * 8 + wn * 4 + j) * 32 + col]);
+  for (int j = 0; j < NB; ++j) Mj[j] = fmaxf(Mj[j], xch[((wm ^ 1) * 8 + wn * NB + j) * 32 + col]);
 
   // 2. e = 2^(z log2 e - m) and its sum (order: i, then r); with Store, e is
   // packed to bf16 and written out as A fragments (see above), one 32x32
   // block at a time to keep few values live.
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int64_t n_ks = Vp / 16;
-  float Sj[4];
+  float Sj[NB];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
+  for (int j = 0; j < NB; ++j) {
     float s = 0.0f;
     // A column whose values are all -inf gets reference +inf: its exponents
     // are -inf and its e exactly 0, with no select per value.
@@ -274,7 +274,7 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
           if (ks < n_ks)
             __builtin_nontemporal_store(
                 f, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(E) +
-                                            frag_offset(tt, ks, wn * 4 + j, n_ks) + lane * 16));
+                                            frag_offset(tt, ks, wn * NB + j, n_ks) + lane * 16));
         }
       }
     }
@@ -283,23 +283,29 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][4], char* ld
   GemmCore::barrier();  // everyone has read the maxima
   if (wm == 1 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) xch[(wn * 4 + j) * 32 + col] = Sj[j];
+    for (int j = 0; j < NB; ++j) xch[(wn * NB + j) * 32 + col] = Sj[j];
   }
   GemmCore::barrier();
   if (wm == 0 && half == 0) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t t = t0 + acc_col(wn, j, lane);
+    for (int j = 0; j < NB; ++j) {
+      const int64_t t = t0 + acc_col(wn, j, lane, NB);
       if (t < T) {
         pm[vt * T + t] = Mj[j];
-        ps[vt * T + t] = Sj[j] + xch[(wn * 4 + j) * 32 + col];
+        ps[vt * T + t] = Sj[j] + xch[(wn * NB + j) * 32 + col];
       }
     }
   }
 }
 
+// Eight waves, two per SIMD (128 x 64 of the tile each): one wave's MFMAs
+// issue while the other of its SIMD waits on LDS, loads or the barrier, and
+// the accumulators live in VGPRs, which the epilogue reads directly.
+constexpr int kFwdWaves = 8;
+
 template <bool Store>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(64 * kFwdWaves)
+__attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
 void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
                   const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
                   int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
@@ -313,10 +319,12 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   if (!tile_of(n_vt, n_tt, vt, tt)) return;
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  GemmCore g;
+  using Core = GemmCoreT<false, false, kFwdWaves>;
+  constexpr int NB = Core::kNB;
+  Core g;
   g.init(W, v0, V, hhat, t0, T, H, lds);
   g.run(H);
-  f32x16 (&acc)[4][4] = g.acc;
+  f32x16 (&acc)[4][NB] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -328,8 +336,8 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   // Target gather: exactly one lane of one workgroup holds z[t, target[t]]
   // (target rows relative to W's first row).
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int64_t t = t0 + acc_col(wn, j, lane);
+  for (int j = 0; j < NB; ++j) {
+    const int64_t t = t0 + acc_col(wn, j, lane, NB);
     if (t < T) {
       const int64_t tg = int64_t(target[t]) - tgt_off;
       const int64_t loc = tg - vbase;
@@ -605,7 +613,12 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
 // Operand A = E (token rows, K = padded vocabulary, in fragment order),
 // operand B = Wt (hidden rows).  The one-hot term is gathered from W exactly
 // in fp32.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+// Four waves, one per SIMD: with the per-fragment exponent shift, two waves
+// per SIMD (8 MFMAs per step over the same A fragments) measured slower.
+constexpr int kDhWaves = 4;
+
+__global__ __launch_bounds__(64 * kDhWaves)
+__attribute__((amdgpu_waves_per_eu(kDhWaves / 4, kDhWaves / 4)))
 void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
                const float* __restrict__ gf, const uint16_t* __restrict__ Wt,
                const uint16_t* __restrict__ W, const int32_t* __restrict__ target,
@@ -616,11 +629,12 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  GemmCoreT<true, true> g;
+  using Core = GemmCoreT<true, true, kDhWaves>;
+  Core g;
   g.init(E, t0, TC, Wt, h0, H, Vp, lds);
   g.set_shift(D, ds, t0, (int64_t(V) + kTile - 1) / kTile);
   g.run(int(Vp));
-  f32x16 (&acc)[4][4] = g.acc;
+  f32x16 (&acc)[4][Core::kNB] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
@@ -637,8 +651,8 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
       const float gt = gf[t];
       const bool ok = tg >= 0 && tg < V;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t h = h0 + acc_col(wn, j, lane);
+      for (int j = 0; j < Core::kNB; ++j) {
+        const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
         if (h < H) {
           const float wt = ok ? bf16_to_f32(W[tg * H + h]) : NAN;
           dh[t * H + h] = c * (wt - gt * acc[i][j][r]);
@@ -1165,11 +1179,11 @@ hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int3
   const int64_t n_tt = ceil_div(T, kTile);
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, NAN);
   if (E)
-    hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
                        ztgt, E);
   else
-    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
                        ztgt, E);
   return hipGetLastError();
@@ -1183,7 +1197,7 @@ hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, cons
   const int64_t n_tt = ceil_div(T, kTile);
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, 0.0f);
   if (n_vt > 0)
-    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, v0, T, H, Vs, n_vt, n_tt, vocab_pad(Vs), pm, ps, ztgt,
                        static_cast<uint16_t*>(nullptr));
   return hipGetLastError();
@@ -1247,7 +1261,7 @@ hipError_t launch_dhidden(const uint16_t* E, const uint32_t* D, int64_t ds, cons
   ProfScope prof("k_dhidden", s);
   const int64_t n_ht = ceil_div(H, kTile);
   const int64_t n_tt = ceil_div(TC, kTile);
-  hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(kThreads), 0, s, E, D, ds, g,
+  hipLaunchKernelGGL(k_dhidden, dim3(raster_grid(n_ht * n_tt)), dim3(64 * kDhWaves), 0, s, E, D, ds, g,
                      Wt, W, target_chunk, coef_chunk, TC, H, V, vocab_pad(V), n_tt, n_ht,
                      dh_chunk);
   return hipGetLastError();
