@@ -1,12 +1,13 @@
 // bf16 MFMA tile core for gfx950 (CDNA4), 64-wide wavefronts.
 //
-// One workgroup of 256 threads (4 waves) computes a 256 x 256 fp32 tile
+// One workgroup computes a 256 x 256 fp32 tile
 //   C[a][b] = sum_k A[a0 + a][k] * B[b0 + b][k]
 // where both operands are row-major with K contiguous ("TN"), the natural
 // layout of hidden states [T,H], the LM-head weight [V,H], a probability
-// block [T,V] and a transposed weight [H,V].  Waves form a 2 x 2 grid, each
-// owning a 128 x 128 sub-tile held as 4 x 4 blocks of the 32x32 output of
-// v_mfma_f32_32x32x16_bf16 (accumulators live in AGPRs).
+// block [T,V] and a transposed weight [H,V].  With 4 waves (256 threads)
+// they form a 2 x 2 grid, each owning a 128 x 128 sub-tile held as 4 x 4
+// blocks of the 32x32 output of v_mfma_f32_32x32x16_bf16 (accumulators in
+// AGPRs); with 8 waves, two per SIMD, each owns 8 blocks (see GemmCoreT).
 //
 // Operand staging.  K is consumed in stages of kBK bf16 (2*kBK bytes per
 // row).  A stage of both operands (2 x 256 rows) is fetched with
@@ -66,11 +67,11 @@ __device__ __forceinline__ uint32_t swz(uint32_t row) {
 }
 
 // Output coordinates of acc[i][j][r] inside the workgroup tile, for lane l of
-// wave (wm, wn) owning nb B blocks (4 with 4 waves, 2 with 8):
-//   a = wm*128 + i*32 + 8*(r/4) + 4*(l/32) + r%4      (operand-A row)
+// wave (wm, wn) owning na A blocks and nb B blocks of 32 rows:
+//   a = wm*32*na + i*32 + 8*(r/4) + 4*(l/32) + r%4    (operand-A row)
 //   b = wn*32*nb + j*32 + l%32                        (operand-B row)
-__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane) {
-  return wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+__device__ __forceinline__ int acc_row(int wm, int i, int r, int lane, int na = 4) {
+  return wm * 32 * na + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
 }
 __device__ __forceinline__ int acc_col(int wn, int j, int lane, int nb = 4) {
   return wn * 32 * nb + j * 32 + (lane & 31);
@@ -131,17 +132,24 @@ __host__ __device__ constexpr int64_t frag_offset(int64_t tile, int64_t ks, int6
 }
 
 // NW: waves per workgroup, 4 (one per SIMD, each owning 128 x 128 of the
-// tile: 4 x 4 blocks) or 8 (two per SIMD, each owning 128 x 64: 4 x 2
-// blocks, accumulators small enough for two waves' registers, so one wave's
-// MFMAs issue while the other waits on LDS, loads or the barrier).  Waves
-// form a 2 x NW/2 grid: wm picks the 128 A rows, wn the 256/(NW/2) B rows.
-template <bool ShiftA, bool ANative = false, int NW = 4>
+// tile: 4 x 4 blocks of 32 x 32) or 8 (two per SIMD, accumulators small
+// enough for two waves' registers, so one wave's MFMAs issue while the other
+// waits on LDS, loads or the barrier).  NA: A blocks per wave (4, or 2 with
+// eight waves: 64 x 128 per wave, half the A fragments to shift per step).
+// Waves form a kWA x kWB grid, wave w at wm = w % kWA (A rows
+// [wm*32*NA, +32*NA)), wn = w / kWA (B rows [wn*32*kNB, +32*kNB)).
+template <bool ShiftA, bool ANative = false, int NW = 4, int NA = 4>
 struct GemmCoreT {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
-  static constexpr int kNB = 16 / NW;                        // B blocks per wave
+  static_assert(NA == 4 || (NA == 2 && NW == 8), "4 A blocks, or 2 with 8 waves");
+  static constexpr int kNA = NA;                             // A blocks per wave
+  static constexpr int kWA = 8 / NA;                         // waves along A
+  static constexpr int kNB = 8 / (NW / kWA);                 // B blocks per wave
   static constexpr int kLP = kTile / kRowsPerLoad / NW;      // loads per wave per operand
-  static constexpr int kNM = 4 * kNB;                        // MFMAs per step
-  static constexpr int kNR = 4 + kNB;                        // fragment reads per step
+  static constexpr int kNM = kNA * kNB;                      // MFMAs per step
+  static constexpr int kNR = kNA + kNB;                      // fragment reads per step
+  __device__ __forceinline__ static int wave_m(int w) { return w % kWA; }
+  __device__ __forceinline__ static int wave_n(int w) { return w / kWA; }
   __amdgpu_buffer_rsrc_t ra, rb;
   uint32_t va[8];            // per-lane byte offsets of the load instructions (B, and A if
                              // row-major); the first kLP are used
@@ -149,20 +157,20 @@ struct GemmCoreT {
   char* smem;
   int wave;
   int nk;                    // number of stages (K / kBK)
-  f32x16 acc[4][kNB];
-  bf16x8 fa[2][4], fb[2][kNB];
+  f32x16 acc[kNA][kNB];
+  bf16x8 fa[2][kNA], fb[2][kNB];
   // ShiftA only: per-lane table pointer (row of block 0), current and next
-  // K block's shifts of the lane's four fragment rows.
+  // K block's shifts of the lane's kNA fragment rows.
   const uint32_t* dsrc;
   int64_t dstride;
   int nq;
-  uint32_t dsh[4], dnxt[4];
+  uint32_t dsh[kNA], dnxt[kNA];
 
   __device__ __forceinline__ void set_shift(const uint32_t* dtab, int64_t stride, int64_t a0,
                                             int64_t n_kblocks) {
     const int lane = threadIdx.x & 63;
-    const int wm = (threadIdx.x >> 6) & 1;
-    dsrc = dtab + a0 + wm * 128 + (lane & 31);
+    const int wm = wave_m(threadIdx.x >> 6);
+    dsrc = dtab + a0 + wm * 32 * kNA + (lane & 31);
     dstride = stride;
     nq = int(n_kblocks);
   }
@@ -174,8 +182,8 @@ struct GemmCoreT {
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform per wave: M0 needs it
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
+    const int wm = wave_m(wave);
+    const int wn = wave_n(wave);
     if (ANative) {
       // the whole fragment block of this 256-row tile (a0 is a multiple of 256)
       const int64_t n_ks = ld / 16;
@@ -202,11 +210,11 @@ struct GemmCoreT {
     // Fragment rows are 32-aligned blocks + lane%32; swz depends on row mod 16.
     const uint32_t r32 = uint32_t(lane & 31);
     const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
-    aoff = ANative ? uint32_t(wm * 4 * 1024 + lane * 16)
-                   : uint32_t(wm * 128 + r32) * kRowBytes + slot0;
+    aoff = ANative ? uint32_t(wm * kNA * 1024 + lane * 16)
+                   : uint32_t(wm * 32 * kNA + r32) * kRowBytes + slot0;
     boff = uint32_t(kOpStageBytes) + uint32_t(wn * 32 * kNB + r32) * kRowBytes + slot0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNA; ++i)
 #pragma unroll
       for (int j = 0; j < kNB; ++j)
 #pragma unroll
@@ -234,10 +242,10 @@ struct GemmCoreT {
   __device__ __forceinline__ void read_one(const char* s, uint32_t oa, uint32_t ob, int q) {
     constexpr int kBlockBytes = 32 * kRowBytes;
     constexpr int kABlockBytes = ANative ? 1024 : kBlockBytes;
-    if (q < 4)
+    if (q < kNA)
       fa[F][q] = *reinterpret_cast<const bf16x8*>(s + oa + q * kABlockBytes);
     else
-      fb[F][q - 4] = *reinterpret_cast<const bf16x8*>(s + ob + (q - 4) * kBlockBytes);
+      fb[F][q - kNA] = *reinterpret_cast<const bf16x8*>(s + ob + (q - kNA) * kBlockBytes);
   }
 
   template <int F>
@@ -249,11 +257,11 @@ struct GemmCoreT {
   // K block of 256 (4 stages of kBK = 64) whose shifts stage kt uses.
   static constexpr int kStagesPerQ = kTile / kBK;
 
-  __device__ __forceinline__ void load_shift(int q, uint32_t (&d)[4]) {
+  __device__ __forceinline__ void load_shift(int q, uint32_t (&d)[kNA]) {
     const int qq = q < nq ? q : nq - 1;
     const uint32_t* p = dsrc + qq * dstride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) d[i] = p[i * 32];
+    for (int i = 0; i < kNA; ++i) d[i] = p[i * 32];
   }
 
   template <int F>
@@ -276,7 +284,7 @@ struct GemmCoreT {
   // flight.  s_waitcnt encoding (gfx9): vmcnt[3:0], expcnt[6:4],
   // lgkmcnt[11:8], vmcnt[5:4] at bits 15:14.
   __device__ __forceinline__ static void wait_loads_except(int stages_after) {
-    const int n = stages_after * 2 * kLoadsPerOp;
+    const int n = stages_after * 2 * kLP;
     switch (n) {
       case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
       case 8: __builtin_amdgcn_s_waitcnt(0x0F70 | 8); break;
@@ -288,7 +296,7 @@ struct GemmCoreT {
   }
 
   // One full MFMA step on set F, reading step kk of stage buffer s into set
-  // F^1 and issuing load pairs of stage lkt (if Load) at MFMAs 0, 4, 8, 12.
+  // F^1 and issuing load pairs of stage lkt (if Load) at every fourth MFMA.
   template <int F, bool Load>
   __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
     const uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
@@ -348,7 +356,7 @@ struct GemmCoreT {
       if (ShiftA) {
         const bool nb = ((kt + 1) % kStagesPerQ) == 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) dsh[i] = nb ? dnxt[i] : dsh[i];
+        for (int i = 0; i < kNA; ++i) dsh[i] = nb ? dnxt[i] : dsh[i];
       }
       shift_frag<0>(0);
       __builtin_amdgcn_sched_barrier(0);

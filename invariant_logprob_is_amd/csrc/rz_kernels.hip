@@ -613,9 +613,11 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
 // Operand A = E (token rows, K = padded vocabulary, in fragment order),
 // operand B = Wt (hidden rows).  The one-hot term is gathered from W exactly
 // in fp32.
-// Four waves, one per SIMD: with the per-fragment exponent shift, two waves
-// per SIMD (8 MFMAs per step over the same A fragments) measured slower.
-constexpr int kDhWaves = 4;
+// Eight waves, two per SIMD, as a 4 x 2 grid of 64 x 128 sub-tiles: two A
+// fragments (token rows) per step carry the exponent shift, half as many as
+// in a 128-row sub-tile.
+constexpr int kDhWaves = 8;
+constexpr int kDhABlocks = 2;
 
 __global__ __launch_bounds__(64 * kDhWaves)
 __attribute__((amdgpu_waves_per_eu(kDhWaves / 4, kDhWaves / 4)))
@@ -629,22 +631,22 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  using Core = GemmCoreT<true, true, kDhWaves>;
+  using Core = GemmCoreT<true, true, kDhWaves, kDhABlocks>;
   Core g;
   g.init(E, t0, TC, Wt, h0, H, Vp, lds);
   g.set_shift(D, ds, t0, (int64_t(V) + kTile - 1) / kTile);
   g.run(int(Vp));
-  f32x16 (&acc)[4][Core::kNB] = g.acc;
+  f32x16 (&acc)[Core::kNA][Core::kNB] = g.acc;
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = Core::wave_m(wave);
+  const int wn = Core::wave_n(wave);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < Core::kNA; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + acc_row(wm, i, r, lane);
+      const int64_t t = t0 + acc_row(wm, i, r, lane, Core::kNA);
       if (t >= TC) continue;
       const int64_t tg = target[t];
       const float c = coef[t];
