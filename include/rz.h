@@ -90,6 +90,28 @@ RZ_API size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
 RZ_API size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
 
 /*
+ * rz_rmsnorm -- the final RMSNorm alone: the first step of rz_logprob.
+ *
+ * The learner and the rollout must run the same forward computation for a
+ * row ([P3] body: batch-invariant kernels and a matching forward pass).  The
+ * pages do not print the norm.  This library takes the usual final RMSNorm:
+ *   r_t     = (mean_k x_tk^2 + eps)^(-1/2)
+ *   hhat_tk = bf16_rne(gamma_k * x_tk * r_t)
+ * evaluated in float64 and rounded once to bf16.  hhat has exactly the bits
+ * that rz_logprob, rz_backward and rz_learner_step feed to the LM head (the
+ * same kernel), and a row's bits depend on that row alone.
+ *
+ * x [T,H] bf16 row-major; gamma [H] bf16; hhat [T,H] bf16 out; rstd [T] fp32
+ * out (r_t rounded to fp32), may be NULL.  x, gamma and hhat 16-byte aligned,
+ * rstd 4-byte aligned.  No workspace.
+ * Errors: RZ_EINVAL (null pointer, misalignment, T < 1, H < 1, eps negative
+ * or NaN), RZ_EUNSUPPORTED (H not a multiple of 64, H > 16384), RZ_ENODEV,
+ * RZ_EHIP.
+ */
+RZ_API int rz_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps,
+                      int64_t T, int32_t H, uint16_t* hhat, float* rstd, void* stream);
+
+/*
  * rz_logprob -- batch-invariant learner log-probabilities.
  *
  * Computes, for every row t < T:

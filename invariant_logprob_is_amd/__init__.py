@@ -46,6 +46,7 @@ SYMBOLS = {
     "rz_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "rz_workspace_bytes": (_SZ, [_I64, _I32, _I32]),
     "rz_workspace_bytes_grads": (_SZ, [_I64, _I32, _I32]),
+    "rz_rmsnorm": (ctypes.c_int, [_P, _P, _F32, _I64, _I32, _P, _P, _P]),
     "rz_logprob": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
@@ -142,6 +143,30 @@ def _workspace(nbytes: int, device, workspace):
     if workspace.numel() < nbytes:
         raise ValueError(f"workspace too small: {workspace.numel()} < {nbytes} bytes")
     return workspace
+
+
+def rmsnorm(x, gamma, eps: float = 1e-6, *, out=None, rstd_out=None):
+    """The final RMSNorm alone (rz_rmsnorm): the hhat bits the LM head of
+    logprob / backward / learner_step consumes.
+
+    x [T,H] bf16, gamma [H] bf16.  Returns (hhat [T,H] bf16, rstd [T] fp32)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    if gamma.shape[0] != H:
+        raise ValueError("shape mismatch between x and gamma")
+    hh = out if out is not None else torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+    rs = rstd_out if rstd_out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    _need(hh, "out", torch.bfloat16, dev, 2)
+    _need(rs, "rstd_out", torch.float32, dev, 1)
+    if tuple(hh.shape) != (T, H) or rs.shape[0] != T:
+        raise ValueError("output shapes do not match x")
+    st = lib().rz_rmsnorm(x.data_ptr(), gamma.data_ptr(), float(eps), T, H, hh.data_ptr(),
+                          rs.data_ptr(), _stream(dev))
+    _check("rz_rmsnorm", st)
+    return hh, rs
 
 
 def logprob(x, gamma, W, target, eps: float = 1e-6, *, workspace=None, out=None,

@@ -50,7 +50,7 @@ hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, cons
   hipError_t e = hipSuccess;
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
-    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, s);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, nullptr, s);
     if (e == hipSuccess)
       e = launch_lmhead_fwd(hhat, W, target + c0, tc, H, V, pm, ps, zt, nullptr, s);
     if (e == hipSuccess)
@@ -74,7 +74,7 @@ hipError_t run_shard(const uint16_t* x, const uint16_t* gamma, float eps, const 
   hipError_t e = hipSuccess;
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
-    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, s);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, nullptr, s);
     if (e == hipSuccess)
       e = launch_lmhead_fwd_range(hhat, W, target + c0, tc, H, v0, Vs, pm, ps, zt, s);
     if (e == hipSuccess)
@@ -130,6 +130,27 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
 
   return status_of(run_logprob(x, gamma, eps, W, target, T, H, V, logprob, lse, workspace, L,
                                static_cast<hipStream_t>(stream)));
+}
+
+int rz_rmsnorm(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T, int32_t H,
+               uint16_t* hhat, float* rstd, void* stream) {
+  if (!x || !gamma || !hhat) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(hhat) || (rstd && !aligned4(rstd)))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  if (T < 1 || H < 1) return RZ_EINVAL;
+  if (H % kHAlign != 0 || H > kMaxH) return RZ_EUNSUPPORTED;
+  const int st = check_device();
+  if (st != RZ_OK) return st;
+  // the same kernel and chunking as the first step of rz_logprob
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipSuccess;
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat + c0 * H, rstd ? rstd + c0 : nullptr,
+                           s);
+  }
+  return status_of(e);
 }
 
 static_assert(RZ_VOCAB_SPLITS == kVocabSplits, "split count");
@@ -292,7 +313,7 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     const int64_t ds = shift_stride(tc);
-    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, s);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
     if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
     if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
     if (e == hipSuccess)
@@ -350,7 +371,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     const int64_t ds = shift_stride(tc);
-    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, s);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
     if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
     if (e == hipSuccess)
       e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse_ + c0, cs + c0,

@@ -135,8 +135,9 @@ struct ProfScope {
 // Kernel launchers (rz_kernels.hip).  All enqueue on `s` and return the
 // launch status (hipGetLastError after the launches).
 // ---------------------------------------------------------------------------
+// rstd (fp32 rounding of the float64 r of each row) may be null.
 hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps,
-                              int64_t T, int H, uint16_t* hhat, hipStream_t s);
+                              int64_t T, int H, uint16_t* hhat, float* rstd, hipStream_t s);
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
                              uint16_t* E, hipStream_t s);

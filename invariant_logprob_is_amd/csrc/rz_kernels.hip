@@ -82,13 +82,15 @@ __device__ __forceinline__ double row_sumsq(const uint16_t* __restrict__ xr, int
 
 __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma, float eps,
-                                                     int64_t T, int H, uint16_t* __restrict__ hhat) {
+                                                     int64_t T, int H, uint16_t* __restrict__ hhat,
+                                                     float* __restrict__ rstd) {
   const int lane = threadIdx.x & 63;
   const int64_t t = int64_t(blockIdx.x) * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
   const uint16_t* xr = x + t * H;
   const double ss = row_sumsq(xr, H, lane);
   const double r = 1.0 / sqrt(ss / double(H) + double(eps));
+  if (rstd && lane == 0) rstd[t] = float(r);
   uint16_t* hr = hhat + t * H;
   for (int c = lane * 8; c < H; c += 64 * 8) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
@@ -1166,10 +1168,10 @@ __global__ __launch_bounds__(256) void k_dgamma_final(const double* __restrict__
 static inline uint32_t blocks_for(int64_t n, int64_t per) { return uint32_t(ceil_div(n, per)); }
 
 hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps, int64_t T,
-                              int H, uint16_t* hhat, hipStream_t s) {
+                              int H, uint16_t* hhat, float* rstd, hipStream_t s) {
   ProfScope prof("k_rmsnorm_fwd", s);
   hipLaunchKernelGGL(k_rmsnorm_fwd, dim3(blocks_for(T, 4)), dim3(256), 0, s, x, gamma, eps, T, H,
-                     hhat);
+                     hhat, rstd);
   return hipGetLastError();
 }
 

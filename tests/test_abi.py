@@ -98,6 +98,28 @@ def _backward(**kw):
                                 a["stream"])
 
 
+def _rmsnorm(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, T=300, H=128, hhat=FAKE, rstd=FAKE, stream=None)
+    a.update(kw)
+    return rz.lib().rz_rmsnorm(a["x"], a["gamma"], a["eps"], a["T"], a["H"], a["hhat"],
+                               a["rstd"], a["stream"])
+
+
+def test_rmsnorm_argument_validation():
+    for k in ("x", "gamma", "hhat"):
+        assert _rmsnorm(**{k: None}) == rz.RZ_EINVAL, k
+    for k in ("x", "gamma", "hhat"):
+        assert _rmsnorm(**{k: FAKE + 8}) == rz.RZ_EINVAL, k   # 16-byte alignment
+    assert _rmsnorm(rstd=FAKE + 2) == rz.RZ_EINVAL
+    assert _rmsnorm(T=0) == rz.RZ_EINVAL
+    assert _rmsnorm(T=-1) == rz.RZ_EINVAL
+    assert _rmsnorm(H=0) == rz.RZ_EINVAL
+    assert _rmsnorm(eps=-1e-6) == rz.RZ_EINVAL
+    assert _rmsnorm(eps=float("nan")) == rz.RZ_EINVAL
+    assert _rmsnorm(H=96) == rz.RZ_EUNSUPPORTED
+    assert _rmsnorm(H=16384 + 64) == rz.RZ_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("fn", [_logprob, _backward])
 def test_head_argument_validation(fn):
     for k in ("x", "gamma", "W", "target", "ws"):
@@ -267,6 +289,8 @@ def test_shard_and_merge_argument_validation():
 
 @pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
 def test_no_device_is_reported():
+    assert _rmsnorm() == rz.RZ_ENODEV
+    assert _rmsnorm(rstd=None) == rz.RZ_ENODEV
     assert _logprob() == rz.RZ_ENODEV
     assert _backward() == rz.RZ_ENODEV
     assert _is_loss() == rz.RZ_ENODEV
