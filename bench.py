@@ -331,7 +331,7 @@ def main():
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU; --gpus above 1 is not supported",
+        print(json.dumps({"error": "the learner head is measured on one GPU; --gpus above 1 is not supported",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
