@@ -138,9 +138,26 @@ __host__ __device__ constexpr int64_t frag_offset(int64_t tile, int64_t ks, int6
 // eight waves: 64 x 128 per wave, half the A fragments to shift per step).
 // Waves form a kWA x kWB grid, wave w at wm = w % kWA (A rows
 // [wm*32*NA, +32*NA)), wn = w / kWA (B rows [wn*32*kNB, +32*kNB)).
-template <bool ShiftA, bool ANative = false, int NW = 4, int NA = 4>
+//
+// Pipe: the stage pipeline.
+//   0: a ring of kStages stages of both operands.  The loads of stage kt+1
+//      are spread over the first two steps of stage kt, and the wait for them
+//      sits halfway through the last step.
+//   1: the same ring.  All of stage kt+1's loads are issued in step 0 and the
+//      wait sits three quarters of the way through the last step, which gives
+//      loads that miss in L2 more time.
+//   2: (A in fragment order, 8 waves) A gets a ring of 3 stages and B one of
+//      2, 160 KB in all.  In step 0 of stage kt the loads of B's stage kt+1
+//      are issued, then those of A's stage kt+2, and the wait at three
+//      quarters of the last step leaves A's stage kt+2 in flight (loads
+//      return in issue order).  An A operand streamed from HBM thus gets
+//      about two stages to arrive instead of one.
+template <bool ShiftA, bool ANative = false, int NW = 4, int NA = 4, int Pipe = 0>
 struct GemmCoreT {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static_assert(Pipe >= 0 && Pipe <= 2, "pipeline 0, 1 or 2");
+  static_assert(Pipe != 2 || (ANative && NW == 8 && kStages == 2),
+                "the deep A ring is built for fragment-order A and 8 waves");
   static_assert(NA == 4 || (NA == 2 && NW == 8), "4 A blocks, or 2 with 8 waves");
   static constexpr int kNA = NA;                             // A blocks per wave
   static constexpr int kWA = 8 / NA;                         // waves along A
@@ -148,6 +165,11 @@ struct GemmCoreT {
   static constexpr int kLP = kTile / kRowsPerLoad / NW;      // loads per wave per operand
   static constexpr int kNM = kNA * kNB;                      // MFMAs per step
   static constexpr int kNR = kNA + kNB;                      // fragment reads per step
+  static constexpr bool kDeep = Pipe == 2;
+  static constexpr int kSplit = Pipe == 0 ? kNM / 2 : kNM * 3 / 4;   // MFMAs before the wait
+  static constexpr int kLds = kDeep ? 5 * kOpStageBytes : kLdsBytes;  // LDS bytes used
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(!kDeep || 2 * kLP <= kNM, "one load per MFMA of step 0");
   __device__ __forceinline__ static int wave_m(int w) { return w % kWA; }
   __device__ __forceinline__ static int wave_n(int w) { return w / kWA; }
   __amdgpu_buffer_rsrc_t ra, rb;
@@ -165,6 +187,8 @@ struct GemmCoreT {
   int64_t dstride;
   int nq;
   uint32_t dsh[kNA], dnxt[kNA];
+  // kDeep only: LDS offsets of this stage's A and B buffers.
+  uint32_t abase_ = 0, bbase_ = 0;
 
   __device__ __forceinline__ void set_shift(const uint32_t* dtab, int64_t stride, int64_t a0,
                                             int64_t n_kblocks) {
@@ -212,7 +236,8 @@ struct GemmCoreT {
     const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
     aoff = ANative ? uint32_t(wm * kNA * 1024 + lane * 16)
                    : uint32_t(wm * 32 * kNA + r32) * kRowBytes + slot0;
-    boff = uint32_t(kOpStageBytes) + uint32_t(wn * 32 * kNB + r32) * kRowBytes + slot0;
+    boff = uint32_t(kDeep ? 3 * kOpStageBytes : kOpStageBytes) +
+           uint32_t(wn * 32 * kNB + r32) * kRowBytes + slot0;
 #pragma unroll
     for (int i = 0; i < kNA; ++i)
 #pragma unroll
@@ -235,6 +260,21 @@ struct GemmCoreT {
                                                0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kOpStageBytes + q * 1024), 16,
                                              va[j], soff, 0, 0);
+  }
+
+  // kDeep: A's and B's instructions of stage kt, each into its own ring.
+  __device__ __forceinline__ void load_a(int kt, int j) {
+    const int q = wave * kLP + j;
+    char* s = smem + (kt % 3) * kOpStageBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
+                                             uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
+                                             kt * kOpStageBytes, 0, 0);
+  }
+  __device__ __forceinline__ void load_b(int kt, int j) {
+    const int q = wave * kLP + j;
+    char* s = smem + (3 + kt % 2) * kOpStageBytes;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + q * 1024), 16, va[j],
+                                             kt * kRowBytes, 0, 0);
   }
 
   // Fragment read number q (0 .. kNR-1) into set F: A blocks first.
@@ -296,17 +336,29 @@ struct GemmCoreT {
   }
 
   // One full MFMA step on set F, reading step kk of stage buffer s into set
-  // F^1 and issuing load pairs of stage lkt (if Load) at every fourth MFMA.
-  template <int F, bool Load>
+  // F^1 and issuing the loads of stage lkt (if Load; and with kDeep, A's
+  // stage lkt+1 if LoadA) as the pipeline places them.
+  template <int F, bool Load, bool LoadA = false>
   __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
-    const uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
-    const uint32_t ob = boff ^ uint32_t(kk << 5);
+    uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
+    uint32_t ob = boff ^ uint32_t(kk << 5);
+    if constexpr (kDeep) {
+      oa += abase_;
+      ob += bbase_;
+    }
 #pragma unroll
     for (int idx = 0; idx < kNM; ++idx) {
       mfma_one<F>(idx);
       if (idx < kNR) read_one<F ^ 1>(s, oa, ob, idx);
-      if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLP)
-        load_pair(lkt, first_pair + (idx >> 2));
+      if constexpr (Pipe == 0) {
+        if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLP)
+          load_pair(lkt, first_pair + (idx >> 2));
+      } else if constexpr (Pipe == 1) {
+        if (Load && first_pair == 0 && idx < kLP) load_pair(lkt, idx);
+      } else {
+        if (Load && first_pair == 0 && idx < kLP) load_b(lkt, idx);
+        if (LoadA && first_pair == 0 && idx >= kLP && idx < 2 * kLP) load_a(lkt + 1, idx - kLP);
+      }
       if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<F>(idx / kNB + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -318,51 +370,64 @@ struct GemmCoreT {
   // the loads of stage kt + kStages - 1 are spread over the first steps; if
   // More, stage kt+1 is waited for and published between the halves of the
   // last step and its step-0 fragments are read during the second half.
-  template <bool Load, bool More>
+  template <bool Load, bool More, bool LoadA = false>
   __device__ __forceinline__ void stage(int kt) {
-    const char* s = smem + (kt % kStages) * kStageBytes;
+    const char* s = kDeep ? smem : smem + (kt % kStages) * kStageBytes;
+    if constexpr (kDeep) {
+      abase_ = uint32_t((kt % 3) * kOpStageBytes);
+      bbase_ = uint32_t((kt % 2) * kOpStageBytes);
+    }
     const int lkt = kt + kStages - 1;
     // The next K block's shifts: issued before this stage's loads, so the
     // wait at the end of the stage covers them too.
     if (ShiftA) load_shift(kt / kStagesPerQ + 1, dnxt);
     // steps 0 .. kSteps-2 (sets alternate 0,1,0,...), each reading the next step
-    step<0, Load>(s, 1, lkt, 0);
+    step<0, Load, LoadA>(s, 1, lkt, 0);
     if (kSteps == 4) {
-      step<1, Load>(s, 2, lkt, kNM / 4);
+      step<1, Load, LoadA>(s, 2, lkt, kNM / 4);
       step<0, false>(s, 3, lkt, 0);
     }
-    // last step (set 1): half its MFMAs, publish stage kt+1, the other half
-    // with the reads of its step 0
+    // last step (set 1): kSplit MFMAs, publish stage kt+1, the rest with the
+    // reads of its step 0
 #pragma unroll
-    for (int idx = 0; idx < kNM / 2; ++idx) {
+    for (int idx = 0; idx < kSplit; ++idx) {
       mfma_one<1>(idx);
       if (idx % kNB == kNB - 1) shift_frag<1>(idx / kNB + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (More) {
-      wait_loads_except(Load ? kStages - 2 : 0);
+      if constexpr (kDeep) {
+        if (LoadA)
+          __builtin_amdgcn_s_waitcnt(0x0F70 | kLP);   // vmcnt(kLP): A's stage kt+2 stays
+        else
+          wait_loads_except(0);
+      } else {
+        wait_loads_except(Load ? kStages - 2 : 0);
+      }
       barrier();
-      const char* sn = smem + ((kt + 1) % kStages) * kStageBytes;
+      const char* sn = kDeep ? smem : smem + ((kt + 1) % kStages) * kStageBytes;
+      const uint32_t na = kDeep ? aoff + uint32_t(((kt + 1) % 3) * kOpStageBytes) : aoff;
+      const uint32_t nb = kDeep ? boff + uint32_t(((kt + 1) % 2) * kOpStageBytes) : boff;
 #pragma unroll
-      for (int idx = kNM / 2; idx < kNM; ++idx) {
+      for (int idx = kSplit; idx < kNM; ++idx) {
         mfma_one<1>(idx);
-        // read u goes with MFMA kNM/2 + u (kNM/2) / kNR: one or two per MFMA
+        // read u goes with MFMA kSplit + u (kNM - kSplit) / kNR
 #pragma unroll
         for (int u = 0; u < kNR; ++u)
-          if (u * (kNM / 2) / kNR == idx - kNM / 2) read_one<0>(sn, aoff, boff, u);
+          if (u * (kNM - kSplit) / kNR == idx - kSplit) read_one<0>(sn, na, nb, u);
         if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<1>(idx / kNB + 1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (ShiftA) {
-        const bool nb = ((kt + 1) % kStagesPerQ) == 0;
+        const bool nq_ = ((kt + 1) % kStagesPerQ) == 0;
 #pragma unroll
-        for (int i = 0; i < kNA; ++i) dsh[i] = nb ? dnxt[i] : dsh[i];
+        for (int i = 0; i < kNA; ++i) dsh[i] = nq_ ? dnxt[i] : dsh[i];
       }
       shift_frag<0>(0);
       __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
-      for (int idx = kNM / 2; idx < kNM; ++idx) {
+      for (int idx = kSplit; idx < kNM; ++idx) {
         mfma_one<1>(idx);
         if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<1>(idx / kNB + 1);
       }
@@ -373,6 +438,40 @@ struct GemmCoreT {
   // trailing barrier, no LDS read outstanding, so the caller may reuse the LDS.
   __device__ __forceinline__ void run(int K) {
     nk = K / kBK;
+    if constexpr (kDeep) {
+      // A's stages 0 and 1 and B's stage 0 in flight; wait for the first two.
+      // The shifts go first, so that waiting for them never waits for A's
+      // stage 1.
+      if (ShiftA) load_shift(0, dsh);
+#pragma unroll
+      for (int j = 0; j < kLP; ++j) load_a(0, j);
+#pragma unroll
+      for (int j = 0; j < kLP; ++j) load_b(0, j);
+      if (nk > 1) {
+#pragma unroll
+        for (int j = 0; j < kLP; ++j) load_a(1, j);
+        __builtin_amdgcn_s_waitcnt(0x0F70 | kLP);
+      } else {
+        wait_loads_except(0);
+      }
+      barrier();
+      // dsh has arrived.  Route it through an empty asm so the compiler
+      // stops treating its registers as a load in flight: it would otherwise
+      // wait at the top of every stage for all older loads, A's next stage
+      // among them.
+      if (ShiftA)
+#pragma unroll
+        for (int i = 0; i < kNA; ++i) asm volatile("" : "+v"(dsh[i]));
+#pragma unroll
+      for (int q = 0; q < kNR; ++q) read_one<0>(smem, aoff, boff, q);
+      shift_frag<0>(0);
+      int kt = 0;
+      for (; kt + 2 < nk; ++kt) stage<true, true, true>(kt);
+      for (; kt + 1 < nk; ++kt) stage<true, true, false>(kt);
+      stage<false, false>(kt);
+      barrier();
+      return;
+    }
     const int pre = nk < kStages - 1 ? nk : kStages - 1;
     for (int st = 0; st < pre; ++st)
 #pragma unroll

@@ -620,6 +620,7 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
 // in a 128-row sub-tile.
 constexpr int kDhWaves = 8;
 constexpr int kDhABlocks = 2;
+constexpr int kDhPipe = 2;   // the deep A ring: e is streamed from HBM
 
 __global__ __launch_bounds__(64 * kDhWaves)
 __attribute__((amdgpu_waves_per_eu(kDhWaves / 4, kDhWaves / 4)))
@@ -628,12 +629,12 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
                const uint16_t* __restrict__ W, const int32_t* __restrict__ target,
                const float* __restrict__ coef, int64_t TC, int H, int V, int64_t Vp,
                int64_t n_tt, int64_t n_ht, float* __restrict__ dh) {
-  __shared__ __attribute__((aligned(16))) char lds[kLdsBytes];
+  using Core = GemmCoreT<true, true, kDhWaves, kDhABlocks, kDhPipe>;
+  __shared__ __attribute__((aligned(16))) char lds[Core::kLds];
   int64_t tt, ht;
   if (!tile_of(n_tt, n_ht, tt, ht)) return;
   const int64_t t0 = tt * kTile;
   const int64_t h0 = ht * kTile;
-  using Core = GemmCoreT<true, true, kDhWaves, kDhABlocks>;
   Core g;
   g.init(E, t0, TC, Wt, h0, H, Vp, lds);
   g.set_shift(D, ds, t0, (int64_t(V) + kTile - 1) / kTile);
