@@ -146,7 +146,7 @@ __host__ __device__ constexpr int64_t frag_offset(int64_t tile, int64_t ks, int6
 //   1: the same ring.  All of stage kt+1's loads are issued in step 0 and the
 //      wait sits three quarters of the way through the last step, which gives
 //      loads that miss in L2 more time.
-//   2: (A in fragment order, 8 waves) A gets a ring of 3 stages and B one of
+//   2: (8 waves) A gets a ring of 3 stages and B one of
 //      2, 160 KB in all.  In step 0 of stage kt the loads of B's stage kt+1
 //      are issued, then those of A's stage kt+2, and the wait at three
 //      quarters of the last step leaves A's stage kt+2 in flight (loads
@@ -156,8 +156,7 @@ template <bool ShiftA, bool ANative = false, int NW = 4, int NA = 4, int Pipe = 
 struct GemmCoreT {
   static_assert(NW == 4 || NW == 8, "4 or 8 waves");
   static_assert(Pipe >= 0 && Pipe <= 2, "pipeline 0, 1 or 2");
-  static_assert(Pipe != 2 || (ANative && NW == 8 && kStages == 2),
-                "the deep A ring is built for fragment-order A and 8 waves");
+  static_assert(Pipe != 2 || (NW == 8 && kStages == 2), "the deep A ring is built for 8 waves");
   static_assert(NA == 4 || (NA == 2 && NW == 8), "4 A blocks, or 2 with 8 waves");
   static constexpr int kNA = NA;                             // A blocks per wave
   static constexpr int kWA = 8 / NA;                         // waves along A
@@ -266,9 +265,13 @@ struct GemmCoreT {
   __device__ __forceinline__ void load_a(int kt, int j) {
     const int q = wave * kLP + j;
     char* s = smem + (kt % 3) * kOpStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
-                                             uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
-                                             kt * kOpStageBytes, 0, 0);
+    if (ANative)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
+                                               uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
+                                               kt * kOpStageBytes, 0, 0);
+    else
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j],
+                                               kt * kRowBytes, 0, 0);
   }
   __device__ __forceinline__ void load_b(int kt, int j) {
     const int q = wave * kLP + j;

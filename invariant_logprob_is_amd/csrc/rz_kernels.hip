@@ -185,7 +185,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 // contraction only carries into rows it does not write.  The stored variant
 // computes M and S with the same code.
 // ---------------------------------------------------------------------------
-constexpr int kFwdLds = kLdsBytes + 2048;  // the GEMM ring + the exchange area
+constexpr int kFwdPipe = 0;
+// The GEMM ring + the exchange area; a ring that fills the LDS holds the
+// exchange area in its last 2 KB, used only after the ring's final barrier.
+constexpr int kFwdLds = kFwdPipe == 2 ? 5 * kOpStageBytes : kLdsBytes + 2048;
 
 // Steps 1-2 of the epilogue and the partials, on the tile's accumulators.
 // Mask: the last vocabulary tile, whose rows v >= V (read as zeros) count as
@@ -321,7 +324,8 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   if (!tile_of(n_vt, n_tt, vt, tt)) return;
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  using Core = GemmCoreT<false, false, kFwdWaves>;
+  using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
+  static_assert(Core::kLds <= kFwdLds, "LDS");
   constexpr int NB = Core::kNB;
   Core g;
   g.init(W, v0, V, hhat, t0, T, H, lds);
