@@ -14,7 +14,8 @@
 // buffer_load_dwordx4 ... lds, which writes straight into LDS without passing
 // through VGPRs; the LDS holds a ring of kStages stages and the loads of stage
 // s are issued while stage s - (kStages - 1) is multiplied, one load pair
-// after every few MFMAs.  Each load instruction moves 1 KB (64 lanes x 16 B,
+// after every few MFMAs (the Pipe parameter of GemmCoreT varies this, and can
+// give A a deeper ring of its own).  Each load instruction moves 1 KB (64 lanes x 16 B,
 // lane-major in LDS); a row's 16-byte chunks are stored XOR-swizzled by a
 // function of the row so that the 16-byte fragment reads of consecutive rows
 // are bank-conflict free whether the LDS serves 8 or 16 lanes x 16 B per
@@ -28,9 +29,9 @@
 // Pipeline per stage (kBK/16 MFMA steps of K=16, 16 MFMAs each): the
 // fragments of the next step are read from LDS while a step multiplies (two
 // fragment register sets, one read after each of the first eight MFMAs); the
-// wait for the next stage and the workgroup barrier sit between the two
-// halves of the last step, so the first fragments of the next stage load
-// while MFMAs run.
+// wait for the next stage and the workgroup barrier sit inside the last step
+// (halfway, or three quarters of the way: Pipe), so the first fragments of
+// the next stage load while MFMAs run.
 //
 // Reduction order: for every output element the K sum is taken in the same
 // fixed order (stage 0, 1, ...; inside a stage steps of 16) no matter which
