@@ -503,12 +503,13 @@ using GemmCore = GemmCoreT<false>;
 // logical order runs all of them side by side for each tile of the first
 // (32 / n_b first-dimension tiles at a time), so each long operand row block
 // of the first streams through one XCD's L2 once.  Otherwise it visits
-// `kRasterGroup` tiles of the first dimension for every tile of the second:
+// `group` tiles of the first dimension for every tile of the second:
 // the group's operand blocks stay in that XCD's L2 while the second
 // dimension's operand streams past, and the workgroups resident on one XCD
 // share both.  The grid is padded to a multiple of 8; returns false for the
 // padding.
-__device__ __forceinline__ bool tile_of(int64_t n_a, int64_t n_b, int64_t& ta, int64_t& tb) {
+__device__ __forceinline__ bool tile_of(int64_t n_a, int64_t n_b, int64_t& ta, int64_t& tb,
+                                        int group = kRasterGroup) {
   const uint64_t nb = gridDim.x;
   const uint64_t b = blockIdx.x;
   const uint64_t w = (b & 7) * (nb >> 3) + (b >> 3);
@@ -520,12 +521,13 @@ __device__ __forceinline__ bool tile_of(int64_t n_a, int64_t n_b, int64_t& ta, i
     tb = int64_t(w % no);
     return true;
   }
-  const uint64_t per_group = uint64_t(kRasterGroup) * no;
+  const uint64_t gr = uint64_t(group);
+  const uint64_t per_group = gr * no;
   const uint64_t g = w / per_group;
   const uint64_t rem = w - g * per_group;
-  const uint64_t left = uint64_t(n_a) - g * kRasterGroup;
-  const uint64_t gsz = left < uint64_t(kRasterGroup) ? left : uint64_t(kRasterGroup);
-  ta = int64_t(g * kRasterGroup + rem % gsz);
+  const uint64_t left = uint64_t(n_a) - g * gr;
+  const uint64_t gsz = left < gr ? left : gr;
+  ta = int64_t(g * gr + rem % gsz);
   tb = int64_t(rem / gsz);
   return true;
 }

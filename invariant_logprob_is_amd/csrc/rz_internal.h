@@ -19,6 +19,22 @@ constexpr int64_t kMaxV = 4000000;  // keeps a 256-row tile of the padded V belo
 constexpr int64_t kBwdChunk = 32768;  // tokens per backward / learner-step chunk (bounds the P workspace)
 constexpr int kRasterGroup = 8;     // first-dimension tiles per L2 group in the tile raster
 
+// Raster group of the forward (vocabulary tiles visited for every token
+// tile).  The forward keeps two things in the MALL (256 MB): the W rows of
+// the current group on each of the 8 XCDs, 8 * g * 256 * H * 2 bytes, and
+// the chunk's hhat, kBwdChunk * H * 2 bytes.  The largest g in {8, 4, 2}
+// whose sum stays within 210 MB is taken.  Measured per step on the forward:
+// at H = 1536, g = 8 beat 4 and 2 by 1% and 3%; at H = 2048, 8 and 4 tied
+// (151 and 168 MB) and 2 lost 2%; at H = 2560, g = 4 (210 MB) beat 8
+// (252 MB) by 8% and 2 by 1.5%.  The grouping only decides which workgroup
+// computes which tile, never a result bit.
+inline int fwd_raster_group(int64_t H) {
+  const int64_t budget = 210LL * 1000 * 1000;
+  for (int g = 8; g > 2; g /= 2)
+    if (H * (8 * int64_t(g) * kTile * 2 + kBwdChunk * 2) <= budget) return g;
+  return 2;
+}
+
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 inline int64_t round_up(int64_t a, int64_t b) { return ceil_div(a, b) * b; }
 inline size_t align256(size_t a) { return (a + 255) & ~size_t(255); }

@@ -314,14 +314,15 @@ __attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
 void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
                   const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
                   int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
-                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E) {
+                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E, int raster_group) {
   __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
   int64_t tt, vt;
-  // Vocabulary tiles are grouped and the token tiles stream past them: the
-  // chunk's hhat (100 MB at H = 1536) stays cache-resident across the
-  // groups, where re-streaming W (467 MB) from HBM for every token group
-  // would not.
-  if (!tile_of(n_vt, n_tt, vt, tt)) return;
+  // Vocabulary tiles are grouped (raster_group of them, chosen on the host
+  // from H so that the group's W rows and the chunk's hhat fit the MALL
+  // together) and the token tiles stream past them: the chunk's hhat
+  // (100 MB at H = 1536) stays cache-resident across the groups, where
+  // re-streaming W (467 MB) from HBM for every token group would not.
+  if (!tile_of(n_vt, n_tt, vt, tt, raster_group)) return;
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
   using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
@@ -1190,11 +1191,11 @@ hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int3
   if (E)
     hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
-                       ztgt, E);
+                       ztgt, E, fwd_raster_group(H));
   else
     hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
-                       ztgt, E);
+                       ztgt, E, fwd_raster_group(H));
   return hipGetLastError();
 }
 
@@ -1208,7 +1209,7 @@ hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, cons
   if (n_vt > 0)
     hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
                        hhat, W, target, v0, T, H, Vs, n_vt, n_tt, vocab_pad(Vs), pm, ps, ztgt,
-                       static_cast<uint16_t*>(nullptr));
+                       static_cast<uint16_t*>(nullptr), fwd_raster_group(H));
   return hipGetLastError();
 }
 
