@@ -91,6 +91,31 @@ def cpu_baseline(b, n_tokens: int):
                       f"D3 and backward to the hidden states in float64 numpy ({dt:.1f} s)"}
 
 
+def side_kernel_bytes(name: str, T: int, H: int, V: int, launches: int):
+    """Algorithmic HBM bytes per step of the head's memory- or latency-bound
+    kernels (what each must read and write at least once), or None for a
+    kernel not listed.  n_vt = ceil(V / 256) vocabulary tiles."""
+    n_vt = -(-V // 256)
+    per = {
+        # x read, hhat written (bf16)
+        "k_rmsnorm_fwd": 4 * H * T,
+        # x read, dhidden read and written in place (fp32)
+        "k_rmsnorm_bwd": 10 * H * T,
+        # per token: the n_vt tile partials (M, S) and z_target, mu and the
+        # float64 token scale read; logprob, lse, coef, the row factor and
+        # the n_vt shifts written
+        "k_lse_combine": (12 * n_vt + 32) * T,
+        # W read, W^T written (bf16)
+        "k_transpose_w": 4 * V * H,
+        # the float64 token scale written
+        "k_token_scale": 8 * T,
+        # logprob and mu read, per launch (the loss; D3 and the KL estimators)
+        "k_is_loss": 8 * T,
+        "k_kl": 8 * T * max(launches, 1),
+    }
+    return per.get(name)
+
+
 CALIBRATION_BYTES = 1 << 28   # plain device-to-device copy run once per benchmark
 
 
@@ -426,6 +451,15 @@ def main():
         achieved = gemm_flops_step * args.steps / (tot / 1000.0)
         kernels[k] = {"ms_per_step": tot / args.steps, "launches_per_step": n // args.steps,
                       "achieved_tflops": achieved / 1e12, "frac": achieved / PEAK_BF16_FLOPS}
+    side = {}
+    for k, (tot, n) in prof.items():
+        nb = side_kernel_bytes(k, T, H, V, n // args.steps)
+        if nb is None or tot <= 0:
+            continue
+        gbs = nb * args.steps / (tot / 1000.0) / 1e9
+        side[k] = {"ms_per_step": tot / args.steps, "launches_per_step": n // args.steps,
+                   "algorithmic_bytes_per_step": nb, "achieved_GBps": gbs,
+                   "frac_of_hbm_peak": gbs * 1e9 / PEAK_HBM_BYTES}
     dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
     roofline = {
         "kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved_tflops"],
@@ -447,6 +481,7 @@ def main():
         "executed_flops_per_token": exec_flops_token,
         "mfma_frac_executed": tokens_per_s * exec_flops_token / PEAK_BF16_FLOPS,
         "kernels": kernels,
+        "side_kernels": side,
         "roofline": roofline,
     }
     if not args.no_cpu_baseline:

@@ -65,16 +65,30 @@ __device__ __forceinline__ double wave_sum(double v) {
 // Each lane accumulates its strided 8-element chunks in a fixed order; the
 // wave then reduces with wave_sum.
 // ---------------------------------------------------------------------------
+// Loads are issued kNormGroup 16-byte chunks per lane at a time before any is
+// used, so a wave has that many in flight instead of one; the arithmetic and
+// its order are those of the plain strided loop.
+constexpr int kNormGroup = 4;
+
 __device__ __forceinline__ double row_sumsq(const uint16_t* __restrict__ xr, int H, int lane) {
   double ss = 0.0;
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+  for (int c0 = lane * 8; c0 < H; c0 += kNormGroup * 512) {
+    u32x4 v[kNormGroup];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double lo = double(__uint_as_float(v[q] << 16));
-      const double hi = double(__uint_as_float(v[q] & 0xFFFF0000u));
-      ss = fma(lo, lo, ss);
-      ss = fma(hi, hi, ss);
+    for (int k = 0; k < kNormGroup; ++k) {
+      const int c = c0 + k * 512;
+      v[k] = c < H ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int k = 0; k < kNormGroup; ++k) {
+      if (c0 + k * 512 >= H) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double lo = double(__uint_as_float(v[k][q] << 16));
+        const double hi = double(__uint_as_float(v[k][q] & 0xFFFF0000u));
+        ss = fma(lo, lo, ss);
+        ss = fma(hi, hi, ss);
+      }
     }
   }
   return wave_sum(ss);
@@ -92,21 +106,32 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict_
   const double r = 1.0 / sqrt(ss / double(H) + double(eps));
   if (rstd && lane == 0) rstd[t] = float(r);
   uint16_t* hr = hhat + t * H;
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
-    u32x4 o;
+  for (int c0 = lane * 8; c0 < H; c0 += kNormGroup * 512) {
+    u32x4 v[kNormGroup], g[kNormGroup];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double xl = double(__uint_as_float(v[q] << 16));
-      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
-      const double gl = double(__uint_as_float(g[q] << 16));
-      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
-      const uint32_t yl = f64_to_bf16_rne((gl * xl) * r);
-      const uint32_t yh = f64_to_bf16_rne((gh * xh) * r);
-      o[q] = yl | (yh << 16);
+    for (int k = 0; k < kNormGroup; ++k) {
+      const int c = c0 + k * 512;
+      const bool in = c < H;
+      v[k] = in ? *reinterpret_cast<const u32x4*>(xr + c) : u32x4{0u, 0u, 0u, 0u};
+      g[k] = in ? *reinterpret_cast<const u32x4*>(gamma + c) : u32x4{0u, 0u, 0u, 0u};
     }
-    *reinterpret_cast<u32x4*>(hr + c) = o;
+#pragma unroll
+    for (int k = 0; k < kNormGroup; ++k) {
+      const int c = c0 + k * 512;
+      if (c >= H) break;
+      u32x4 o;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double xl = double(__uint_as_float(v[k][q] << 16));
+        const double xh = double(__uint_as_float(v[k][q] & 0xFFFF0000u));
+        const double gl = double(__uint_as_float(g[k][q] << 16));
+        const double gh = double(__uint_as_float(g[k][q] & 0xFFFF0000u));
+        const uint32_t yl = f64_to_bf16_rne((gl * xl) * r);
+        const uint32_t yh = f64_to_bf16_rne((gh * xh) * r);
+        o[q] = yl | (yh << 16);
+      }
+      *reinterpret_cast<u32x4*>(hr + c) = o;
+    }
   }
 }
 
@@ -114,8 +139,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_fwd(const uint16_t* __restrict_
 // RMSNorm backward, in place on dh (fp32), one wave per row.
 //   dx_j = r gamma_j g_j - x_j r^3 (1/H) sum_k gamma_k g_k x_k
 // r is recomputed with the forward's exact code (row_sumsq), so it has the
-// forward's bits.
+// forward's bits.  Loads are grouped as in the forward.
 // ---------------------------------------------------------------------------
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict__ x,
                                                      const uint16_t* __restrict__ gamma, float eps,
                                                      int64_t T, int H, float* __restrict__ dh) {
@@ -126,33 +153,62 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
   float* gr = dh + t * H;
   const double ss = row_sumsq(xr, H, lane);
   const double r = 1.0 / sqrt(ss / double(H) + double(eps));
+  // the 8 values of chunk c: x, gamma (bf16) and dh (fp32, two 16-byte halves)
+  auto load = [&](int c, u32x4& v, u32x4& g, f32x4& d0, f32x4& d1) {
+    v = *reinterpret_cast<const u32x4*>(xr + c);
+    g = *reinterpret_cast<const u32x4*>(gamma + c);
+    d0 = *reinterpret_cast<const f32x4*>(gr + c);
+    d1 = *reinterpret_cast<const f32x4*>(gr + c + 4);
+  };
   double sg = 0.0;
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
+  for (int c0 = lane * 8; c0 < H; c0 += kNormGroup * 512) {
+    u32x4 v[kNormGroup], g[kNormGroup];
+    f32x4 d0[kNormGroup], d1[kNormGroup];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double xl = double(__uint_as_float(v[q] << 16));
-      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
-      const double gl = double(__uint_as_float(g[q] << 16));
-      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
-      sg = fma(gl * double(gr[c + 2 * q]), xl, sg);
-      sg = fma(gh * double(gr[c + 2 * q + 1]), xh, sg);
+    for (int k = 0; k < kNormGroup; ++k)
+      if (c0 + k * 512 < H) load(c0 + k * 512, v[k], g[k], d0[k], d1[k]);
+#pragma unroll
+    for (int k = 0; k < kNormGroup; ++k) {
+      if (c0 + k * 512 >= H) break;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double xl = double(__uint_as_float(v[k][q] << 16));
+        const double xh = double(__uint_as_float(v[k][q] & 0xFFFF0000u));
+        const double gl = double(__uint_as_float(g[k][q] << 16));
+        const double gh = double(__uint_as_float(g[k][q] & 0xFFFF0000u));
+        const float dl = q < 2 ? d0[k][2 * q] : d1[k][2 * q - 4];
+        const float dhh = q < 2 ? d0[k][2 * q + 1] : d1[k][2 * q - 3];
+        sg = fma(gl * double(dl), xl, sg);
+        sg = fma(gh * double(dhh), xh, sg);
+      }
     }
   }
   sg = wave_sum(sg);
   const double c3 = r * r * r * sg / double(H);
-  for (int c = lane * 8; c < H; c += 64 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
-    const u32x4 g = *reinterpret_cast<const u32x4*>(gamma + c);
+  for (int c0 = lane * 8; c0 < H; c0 += kNormGroup * 512) {
+    u32x4 v[kNormGroup], g[kNormGroup];
+    f32x4 d0[kNormGroup], d1[kNormGroup];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const double xl = double(__uint_as_float(v[q] << 16));
-      const double xh = double(__uint_as_float(v[q] & 0xFFFF0000u));
-      const double gl = double(__uint_as_float(g[q] << 16));
-      const double gh = double(__uint_as_float(g[q] & 0xFFFF0000u));
-      gr[c + 2 * q] = float(r * gl * double(gr[c + 2 * q]) - xl * c3);
-      gr[c + 2 * q + 1] = float(r * gh * double(gr[c + 2 * q + 1]) - xh * c3);
+    for (int k = 0; k < kNormGroup; ++k)
+      if (c0 + k * 512 < H) load(c0 + k * 512, v[k], g[k], d0[k], d1[k]);
+#pragma unroll
+    for (int k = 0; k < kNormGroup; ++k) {
+      const int c = c0 + k * 512;
+      if (c >= H) break;
+      float o[8];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const double xl = double(__uint_as_float(v[k][q] << 16));
+        const double xh = double(__uint_as_float(v[k][q] & 0xFFFF0000u));
+        const double gl = double(__uint_as_float(g[k][q] << 16));
+        const double gh = double(__uint_as_float(g[k][q] & 0xFFFF0000u));
+        const float dl = q < 2 ? d0[k][2 * q] : d1[k][2 * q - 4];
+        const float dhh = q < 2 ? d0[k][2 * q + 1] : d1[k][2 * q - 3];
+        o[2 * q] = float(r * gl * double(dl) - xl * c3);
+        o[2 * q + 1] = float(r * gh * double(dhh) - xh * c3);
+      }
+      *reinterpret_cast<f32x4*>(gr + c) = f32x4{o[0], o[1], o[2], o[3]};
+      *reinterpret_cast<f32x4*>(gr + c + 4) = f32x4{o[4], o[5], o[6], o[7]};
     }
   }
 }
