@@ -14,7 +14,7 @@ from gpu_util import bf16, host, i32, say
 
 pytestmark = pytest.mark.gpu
 
-# Input rows come from seed streams of their own (master seeds 11-16), apart
+# Input rows come from seed streams of their own (master seeds 11-17), apart
 # from the workloads' (0-4).
 
 
@@ -82,6 +82,10 @@ def test_workload_shaped_rows(rz, gpu):
     xf[rows] *= np.float32(20.0)
     x = workloads.f32_to_bf16_bits(xf)
     _check_against_oracle(rz, gpu, x, g30, 1e-6, "30B-head-shaped rows with outliers")
+    # 4B-shaped rows (H = 2560) with that workload's gamma
+    g4 = workloads.qwen4b_lag64(with_W=False, with_x=False).gamma
+    x, _ = workloads.rows_only(17, 1, 2048, 2560, 151936)
+    _check_against_oracle(rz, gpu, x, g4, 1e-6, "4B-shaped rows")
 
 
 @pytest.mark.parametrize("H", [64, 16384])
