@@ -352,6 +352,8 @@ def main():
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/traffic_<kernel>.json and exit")
     args = ap.parse_args()
+    if args.steps < 1 or args.warmup < 0 or args.cpu_tokens < 1:
+        ap.error("--steps and --cpu-tokens must be at least 1, --warmup at least 0")
     if args.summarize_counters:
         summarize_counters(*args.summarize_counters)
         return
