@@ -117,6 +117,60 @@ def side_kernel_bytes(name: str, T: int, H: int, V: int, launches: int):
 
 
 CALIBRATION_BYTES = 1 << 28   # plain device-to-device copy run once per benchmark
+NOMINAL_SCLK_MHZ = 2400.0     # the shader clock the published MFMA peak assumes
+
+
+class SclkSampler:
+    """Reads the GPU's current shader clock (the starred line of the amdgpu
+    driver's pp_dpm_sclk in sysfs) every 50 ms on a side thread while the
+    timed steps run.  Reports nothing when the file is absent, or when there
+    is more than one GPU and the one in use cannot be told apart."""
+
+    def __init__(self, interval_s: float = 0.05):
+        import glob
+        import threading
+        files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = files[0] if len(files) == 1 else None
+        self.interval = interval_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        import re
+        try:
+            with open(self.path) as f:
+                for line in f:
+                    m = re.search(r"(\d+)\s*Mhz\s*\*", line, re.I)
+                    if m:
+                        return float(m.group(1))
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.interval)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.path:
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        v = np.asarray(self.samples)
+        return {"mean_mhz": float(v.mean()), "min_mhz": float(v.min()), "max_mhz": float(v.max()),
+                "samples": int(v.size), "source": self.path}
 
 
 def summarize_counters(fetch_csv: str, write_csv: str):
@@ -426,13 +480,14 @@ def main():
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     rz.profile_enable(True)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev[0].record(stream)
-    for i in range(args.steps):
-        step()
-        ev[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with SclkSampler() as sclk:
+        t0 = time.perf_counter()
+        ev[0].record(stream)
+        for i in range(args.steps):
+            step()
+            ev[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     prof = rz.profile_read()
     rz.profile_enable(False)
     step_ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]
@@ -486,6 +541,12 @@ def main():
         "side_kernels": side,
         "roofline": roofline,
     }
+    clock = sclk.summary()
+    if clock is not None:
+        # the same algorithmic rate against the peak at the clock the chip held
+        clock["mfma_frac_algorithmic_at_this_clock"] = (
+            out["mfma_frac_algorithmic"] * NOMINAL_SCLK_MHZ / clock["mean_mhz"])
+        out["sclk_during_timed_steps"] = clock
     if not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_tokens} tokens ...")
         cb = cpu_baseline(b, args.cpu_tokens)
