@@ -388,7 +388,7 @@ PROBE_MODES = {0: "zeros", 1: "random bf16 with the exponents of normal(0, 1) da
                2: "random bf16 with the magnitudes of LM-head weights and of e"}
 
 
-def run_mfma_peak(args, torch, rz):
+def run_mfma_peak(torch, rz):
     """The register-only bf16 MFMA rate by operand data (rz_probe_mfma_peak),
     with the shader clock sampled during each timed launch."""
     import ctypes
@@ -469,7 +469,7 @@ def main():
 
     rz.lib()
     if args.mfma_peak:
-        run_mfma_peak(args, torch, rz)
+        run_mfma_peak(torch, rz)
         return
     dev = torch.device("cuda", 0)
     t_gen = time.perf_counter()
