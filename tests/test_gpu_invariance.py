@@ -39,3 +39,29 @@ def test_invariance_sweep_15b(gpu):
         np.testing.assert_array_equal(c, seen[ref_label][1], err_msg=f"lse bits {label}")
     lp = seen[ref_label][0].view(np.float32)
     assert np.all(np.isfinite(lp)) and np.all(lp <= 0)
+
+
+# The forward's raster group depends on H (8 vocabulary tiles up to
+# H = 2048, 4 at 2560, 2 beyond) and is used once a batch has more than 32
+# token tiles (8192 rows).  It decides only which workgroup computes which
+# tile, so a row's bits must not depend on it: rows alone and inside a
+# 9000-row batch, at the hidden sizes that select each group.
+@pytest.mark.parametrize("H", [1536, 2560, 3072])
+def test_invariance_across_raster_groups(gpu, H):
+    import invariant_logprob_is_amd as rz
+    V, n, B = 1000, 40, 9000
+    say(f"raster-group invariance H={H}: {n} rows alone and inside a {B}-row batch")
+    xb, tb = workloads.rows_only(18, 1, n, H, V)
+    fx, ft = workloads.rows_only(19, 1, B, H, V)
+    rng = np.random.default_rng(H)
+    g = bf16(workloads.f32_to_bf16_bits((1 + 0.1 * rng.standard_normal(H)).astype(np.float32)), gpu)
+    W = bf16(workloads.f32_to_bf16_bits((0.02 * rng.standard_normal((V, H))).astype(np.float32)), gpu)
+    alone = [rz.logprob(bf16(xb[i:i + 1], gpu), g, W, i32(tb[i:i + 1], gpu)) for i in range(n)]
+    ref_lp = np.concatenate([bits32(a[0]) for a in alone])
+    ref_lse = np.concatenate([bits32(a[1]) for a in alone])
+    pos = np.sort(rng.choice(B, n, replace=False))
+    bx, bt = fx.copy(), ft.copy()
+    bx[pos], bt[pos] = xb, tb
+    lp, lse = rz.logprob(bf16(bx, gpu), g, W, i32(bt, gpu))
+    np.testing.assert_array_equal(bits32(lp)[pos], ref_lp)
+    np.testing.assert_array_equal(bits32(lse)[pos], ref_lse)
