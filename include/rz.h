@@ -35,8 +35,13 @@
  *     before any HIP call, so argument errors are reported on machines
  *     without a GPU.  Data that lives on the device (targets, offsets) is
  *     not inspected on the host: an out-of-range target yields NaN for that
- *     token's log-probability, and malformed offsets yield a NaN loss.
- *   - Determinism: no atomics; outputs are bitwise identical run to run.
+ *     token's log-probability (and gradient row), and malformed offsets are
+ *     detected on the device and yield NaN for the loss and every coef.
+ *   - Determinism: outputs are bitwise identical run to run.  Every
+ *     floating-point sum runs in a fixed order; the only atomics are integer
+ *     counts (the digit histograms of the weight gradient's bucketing),
+ *     whose totals do not depend on the order, and each entry's place in a
+ *     bucket is fixed by its token index, not by arrival.
  *   - Layout: row t pairs the final hidden state that predicts target[t] with
  *     that target (the caller applies the next-token shift and drops prompt
  *     tokens).  Tokens of a response are contiguous; the responses of one
@@ -83,8 +88,9 @@ RZ_API size_t rz_workspace_bytes(int64_t T, int32_t H, int32_t V);
 /*
  * rz_workspace_bytes_grads -- workspace for rz_learner_step with the weight
  * gradients (dW, dgamma): the above plus one chunk of scaled hidden states
- * (32768 x H bf16), the per-chunk target buckets and the dgamma partials
- * (about 120 MB more at H = 1536, V = 151,936 and T = 584,025).
+ * (32768 x H bf16), the sort buffers and partial sums of the per-row exact
+ * terms, and the dgamma partials (about 200 MB more at H = 1536,
+ * V = 151,936 and T = 584,025).
  * 0 for invalid sizes.
  */
 RZ_API size_t rz_workspace_bytes_grads(int64_t T, int32_t H, int32_t V);
@@ -159,9 +165,10 @@ RZ_API int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
  * group_offsets [G+1] int64 response offsets of the prompt groups
  * (group_offsets[0] = 0, group_offsets[G] = R, strictly increasing);
  * reward [R] fp32.  Outputs: loss [1] fp64; coef [T] fp32 (may be NULL);
- * advantage [R] fp32 (may be NULL).  Offsets are read on the device: a
- * malformed structure writes NaN to loss (and to the coef of the affected
- * responses); no out-of-bounds access happens.
+ * advantage [R] fp32 (may be NULL).  Offsets are read on the device and
+ * checked there first: a malformed structure (offsets that do not start at
+ * 0, do not end at T or R, or do not strictly increase) writes NaN to loss,
+ * to every coef and to every advantage; no out-of-bounds access happens.
  * Errors: RZ_EINVAL (null pointer, T < 1, R < 1, G < 1, R > T, G > R),
  * RZ_EWORKSPACE, RZ_ENODEV, RZ_EHIP.
  */
@@ -306,8 +313,13 @@ RZ_API int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const 
  * per 256-wide vocabulary tile, then contracted with W on bf16 MFMA with fp32
  * accumulation in a fixed vocabulary order, p = e 2^(m_j - m) exp(m ln 2 -
  * lse) being applied as an exact exponent shift of e inside the contraction
- * and a per-token factor after it), followed by the RMSNorm backward in
- * fp64/fp32, the bf16 rounding of hhat being treated as the identity:
+ * and a per-token factor after it).  The row's dominant probabilities are
+ * then made exact: with p_t the target's, the target and the 8 largest p_tv
+ * that reach 2^-10 (1 - p_t) have z recomputed in fp64 from hhat and W, and
+ * their bf16 terms in the contraction are replaced by the exact ones, so a
+ * row whose softmax is peaked (a token sampled from the policy itself) keeps
+ * the accuracy of a flat one.  The RMSNorm backward follows in fp64/fp32, the
+ * bf16 rounding of hhat being treated as the identity:
  *   dx_j = r gamma_j g_j - x_j r^3 (1/H) sum_k gamma_k g_k x_k.
  *
  * x, gamma, eps, W, target as for rz_logprob; lse, coef [T] fp32;
@@ -349,10 +361,14 @@ RZ_API int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
  *   dgamma[k] = sum_t dhhat_tk x_tk r_t                          [H] fp32
  * (the bf16 rounding of hhat is straight-through).  The softmax part is
  * contracted on bf16 MFMA from coef_t p_tv rounded once to bf16, fp32
- * accumulation, chunks added in order; the one-hot part is added exactly in
- * fp32, per target row in token order; dgamma is summed in float64 in a
- * fixed order.  Deterministic run to run.  They need the larger workspace
- * of rz_workspace_bytes_grads.
+ * accumulation, chunks added in order; the one-hot part and the exact terms
+ * of each token's dominant probabilities (those of rz_backward) are added in
+ * fp32, per vocabulary row in token order; dgamma is summed in float64 in a
+ * fixed order.  Deterministic run to run.  dW must be 16-byte aligned.  They
+ * need the larger workspace of rz_workspace_bytes_grads.
+ * A malformed response structure gives NaN for the loss, every coef, every
+ * dhidden row and the weight gradients; logprob, lse, d3 and kl do not
+ * depend on it.
  * Errors: the union of those of rz_logprob and rz_is_loss; RZ_EINVAL also for
  * exactly one of dW, dgamma NULL.
  */

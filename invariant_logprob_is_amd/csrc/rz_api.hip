@@ -214,7 +214,8 @@ int rz_is_loss(const float* logprob, const float* rollout_logprob, int64_t T,
   if (st != RZ_OK) return st;
   hipStream_t s = static_cast<hipStream_t>(stream);
   return status_of(launch_is_loss(logprob, rollout_logprob, T, resp_offsets, R, group_offsets, G,
-                                  reward, loss, coef, advantage, at<double>(workspace, L.part), s));
+                                  reward, loss, coef, advantage, at<double>(workspace, L.part),
+                                  at<int>(workspace, L.flag), true, s));
 }
 
 int rz_d3(const float* logprob, const float* rollout_logprob, int64_t T, double* d3,
@@ -309,6 +310,7 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
   float* zt = at<float>(workspace, L.b_zt);
   uint32_t* D = at<uint32_t>(workspace, L.b_d);
   float* g = at<float>(workspace, L.b_g);
+  SelRec* rec = at<SelRec>(workspace, L.b_rec);
   hipError_t e = launch_transpose_w(W, H, V, Wt, s);
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
@@ -317,7 +319,11 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
     if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
     if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
     if (e == hipSuccess)
+      e = launch_select(pm, tc, V, lse + c0, zt, target + c0, coef + c0, D, ds, g, E, hh, W, H,
+                        rec, s);
+    if (e == hipSuccess)
       e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
+    if (e == hipSuccess) e = launch_dh_fix(rec, coef + c0, W, tc, H, dhidden + c0 * H, s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
   return status_of(e);
@@ -341,7 +347,7 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     return RZ_EINVAL;
   if (!(eps >= 0.0f)) return RZ_EINVAL;
   if ((dW == nullptr) != (dgamma == nullptr)) return RZ_EINVAL;
-  if ((dW && !aligned4(dW)) || (dgamma && !aligned4(dgamma))) return RZ_EINVAL;
+  if ((dW && !aligned16(dW)) || (dgamma && !aligned4(dgamma))) return RZ_EINVAL;
   int st = check_head_shape(T, H, V);
   if (st != RZ_OK) return st;
   if (R < 1 || G < 1 || int64_t(R) > T || G > R) return RZ_EINVAL;
@@ -360,14 +366,16 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
   float* zt = at<float>(workspace, L.s_zt);
   uint32_t* D = at<uint32_t>(workspace, L.s_d);
   float* g = at<float>(workspace, L.s_g);
+  SelRec* rec = at<SelRec>(workspace, L.s_rec);
   double* cs = at<double>(workspace, L.s_cs);
   float* lse_ = lse ? lse : at<float>(workspace, L.s_lse);
   float* coef_ = coef ? coef : at<float>(workspace, L.s_coef);
   double* part = at<double>(workspace, L.s_part);
+  int* ok = at<int>(workspace, L.s_flag);
 
   hipError_t e = launch_transpose_w(W, H, V, Wt, s);
   if (e == hipSuccess)
-    e = launch_token_scale(resp_offsets, R, group_offsets, G, reward, T, cs, s);
+    e = launch_token_scale(resp_offsets, R, group_offsets, G, reward, T, ok, cs, s);
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     const int64_t ds = shift_stride(tc);
@@ -377,18 +385,24 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
       e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse_ + c0, cs + c0,
                              rollout_logprob + c0, coef_ + c0, D, ds, g, s);
     if (e == hipSuccess)
+      e = launch_select(pm, tc, V, lse_ + c0, zt, target + c0, coef_ + c0, D, ds, g, E, hh, W, H,
+                        rec, s);
+    if (e == hipSuccess)
       e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef_ + c0, tc, H, V, dhidden + c0 * H,
                          s);
+    if (e == hipSuccess) e = launch_dh_fix(rec, coef_ + c0, W, tc, H, dhidden + c0 * H, s);
     if (e == hipSuccess && grads)
       e = launch_weight_grads_chunk(E, D, ds, g, coef_ + c0, target + c0, hh, x + c0 * H, eps,
                                     dhidden + c0 * H, tc, H, V, c0 / kTile, c0 == 0,
-                                    at<uint16_t>(workspace, L.g_hs), at<int32_t>(workspace, L.g_ibuf),
+                                    at<uint16_t>(workspace, L.g_hs), rec,
+                                    dw_exact_bufs(at<char>(workspace, L.g_dw), tc, H),
+                                    at<double>(workspace, L.g_rbuf),
                                     at<double>(workspace, L.g_part), dW, s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
   if (e == hipSuccess)
     e = launch_is_loss(logprob, rollout_logprob, T, resp_offsets, R, group_offsets, G, reward,
-                       loss, nullptr, nullptr, part, s);
+                       loss, nullptr, nullptr, part, ok, false, s);
   if (e == hipSuccess) e = launch_d3(logprob, rollout_logprob, T, d3, part, s);
   if (e == hipSuccess && kl) e = launch_kl(logprob, rollout_logprob, T, kl, part, s);
   if (e == hipSuccess && grads)

@@ -5,6 +5,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "rz_util.h"
+
 namespace rz {
 
 // ---------------------------------------------------------------------------
@@ -57,19 +59,63 @@ inline int64_t split_first_row(int64_t V, int s) {
 // 256-row token tiles, so the contraction reads it without a bounds check.
 inline int64_t shift_stride(int64_t tc) { return round_up(tc, kTile); }
 
+// Buffers of the weight gradient's exact entries (rz_exact.hip) for a chunk
+// of tc tokens: per token kEntPerToken entries at most (the one-hot entry and
+// the kSelSlots records), sorted by vocabulary row with an LSD radix sort of
+// kRsItemsPerBlock keys per block; the partial sums of buckets that span
+// blocks of 64 sorted positions, two per block.
+constexpr int kEntPerToken = kSelSlots + 1;
+constexpr int kRsItemsPerBlock = 2048;
+struct DwExactBufs {
+  int32_t* keys[2];
+  int32_t* vals[2];
+  int32_t* off;     // per-token entry offsets; off[tc] = the entry count
+  int32_t* hist;    // 256 digit counts per sort block
+  float* seg;       // 2 partial rows of H per block of 64 sorted positions
+};
+inline int64_t dw_exact_nmax(int64_t tc) { return tc * kEntPerToken; }
+inline size_t dw_exact_bytes(int64_t tc, int64_t H) {
+  const int64_t n = dw_exact_nmax(tc);
+  const int64_t nblk = (n + kRsItemsPerBlock - 1) / kRsItemsPerBlock;
+  const int64_t nseg = (n + 63) / 64;
+  size_t o = 0;
+  for (int i = 0; i < 4; ++i) o = align256(o + size_t(n) * 4);
+  o = align256(o + size_t(tc + 1) * 4);
+  o = align256(o + size_t(256) * nblk * 4);
+  o = align256(o + size_t(2) * nseg * H * 4);
+  return o;
+}
+inline DwExactBufs dw_exact_bufs(void* base, int64_t tc, int64_t H) {
+  (void)H;
+  const int64_t n = dw_exact_nmax(tc);
+  const int64_t nblk = (n + kRsItemsPerBlock - 1) / kRsItemsPerBlock;
+  char* b = static_cast<char*>(base);
+  DwExactBufs w;
+  size_t o = 0;
+  w.keys[0] = reinterpret_cast<int32_t*>(b + o); o = align256(o + size_t(n) * 4);
+  w.vals[0] = reinterpret_cast<int32_t*>(b + o); o = align256(o + size_t(n) * 4);
+  w.keys[1] = reinterpret_cast<int32_t*>(b + o); o = align256(o + size_t(n) * 4);
+  w.vals[1] = reinterpret_cast<int32_t*>(b + o); o = align256(o + size_t(n) * 4);
+  w.off = reinterpret_cast<int32_t*>(b + o);     o = align256(o + size_t(tc + 1) * 4);
+  w.hist = reinterpret_cast<int32_t*>(b + o);    o = align256(o + size_t(256) * nblk * 4);
+  w.seg = reinterpret_cast<float*>(b + o);
+  return w;
+}
+
 // Workspace layout; every region starts on a 256-byte boundary.  Regions of
 // different entry points overlap (calls on one workspace are ordered).
 struct WsLayout {
   // rz_logprob (chunks of at most kBwdChunk tokens)
   size_t hhat, pm, ps, ztgt, fwd_end;
   // rz_backward (chunks of at most kBwdChunk tokens)
-  size_t b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, bwd_end;
+  size_t b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, b_rec, bwd_end;
   // rz_is_loss / rz_d3
-  size_t part, loss_end;
+  size_t part, flag, loss_end;
   // rz_learner_step (chunks of at most kBwdChunk tokens)
-  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_cs, s_lse, s_coef, s_part, step_end;
+  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_rec, s_cs, s_lse, s_coef, s_part,
+      s_flag, step_end;
   // rz_learner_step with weight gradients: the step region, then these
-  size_t g_hs, g_ibuf, g_part, grads_end;
+  size_t g_hs, g_dw, g_rbuf, g_part, grads_end;
   size_t total;
 };
 
@@ -94,9 +140,11 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.b_zt = o;   o = align256(o + size_t(tc) * 4);
   L.b_d = o;    o = align256(o + size_t(nvt) * tcp * 4);
   L.b_g = o;    o = align256(o + size_t(tc) * 4);
+  L.b_rec = o;  o = align256(o + size_t(tc) * kSelSlots * sizeof(SelRec));
   L.bwd_end = o;
   o = 0;
   L.part = o;   o = align256(o + size_t(T + 8) * 8);
+  L.flag = o;   o = align256(o + 4);
   L.loss_end = o;
   o = 0;
   L.s_hhat = o; o = align256(o + size_t(tc) * H * 2);
@@ -107,17 +155,18 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.s_zt = o;   o = align256(o + size_t(tc) * 4);
   L.s_d = o;    o = align256(o + size_t(nvt) * tcp * 4);
   L.s_g = o;    o = align256(o + size_t(tc) * 4);
+  L.s_rec = o;  o = align256(o + size_t(tc) * kSelSlots * sizeof(SelRec));
   L.s_cs = o;   o = align256(o + size_t(T) * 8);
   L.s_lse = o;  o = align256(o + size_t(T) * 4);
   L.s_coef = o; o = align256(o + size_t(T) * 4);
   L.s_part = o; o = align256(o + size_t(T + 8) * 8);
+  L.s_flag = o; o = align256(o + 4);
   L.step_end = o;
   // the chunk's hhat rows scaled by coef_t g_t (bf16), token-contiguous
   L.g_hs = o;   o = align256(o + size_t(H) * tcp * 2);
-  // count, cursor, offsets, bucket slots, sorted order, scan block totals;
-  // then the chunk's row factors r_t (float64)
-  L.g_ibuf = o; o = align256(o + align256(size_t(3 * V + 1 + 2 * tc + ceil_div(V, 1024) + 1) * 4)
-                            + size_t(tc) * 8);
+  // the sort and sums of the exact entries; then the chunk's row factors r_t
+  L.g_dw = o;   o = align256(o + dw_exact_bytes(tc, H));
+  L.g_rbuf = o; o = align256(o + size_t(tc) * 8);
   L.g_part = o; o = align256(o + size_t(ceil_div(T, kTile)) * H * 8);
   L.grads_end = o;
   L.total = L.fwd_end;
@@ -179,8 +228,12 @@ hipError_t launch_lse_combine(const float* pm, const float* ps, const float* ztg
                               hipStream_t s);
 hipError_t launch_shift_prep(const float* pm, const float* lse, int64_t T, int V, uint32_t* D,
                              int64_t ds, float* g, hipStream_t s);
+// Checks the ragged structure into *ok (an int in device memory), then
+// writes the token scale (NaN for every token when the structure is
+// malformed).
 hipError_t launch_token_scale(const int64_t* ro, int R, const int64_t* go, int G,
-                              const float* reward, int64_t T, double* cs, hipStream_t s);
+                              const float* reward, int64_t T, int* ok, double* cs,
+                              hipStream_t s);
 hipError_t launch_transpose_w(const uint16_t* W, int H, int V, uint16_t* Wt, hipStream_t s);
 hipError_t launch_dhidden(const uint16_t* E, const uint32_t* D, int64_t ds, const float* g,
                           const uint16_t* Wt, const uint16_t* W, const int32_t* target_chunk,
@@ -188,19 +241,36 @@ hipError_t launch_dhidden(const uint16_t* E, const uint32_t* D, int64_t ds, cons
                           hipStream_t s);
 hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float eps,
                               int64_t T, int H, float* dh, hipStream_t s);
+// The loss, coef and advantages; with check, the structure flag *ok is
+// computed first, otherwise it is the one launch_token_scale computed.
 hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T,
                           const int64_t* ro, int R, const int64_t* go, int G,
                           const float* reward, double* loss, float* coef, float* adv,
-                          double* part, hipStream_t s);
+                          double* part, int* ok, bool check, hipStream_t s);
 hipError_t launch_d3(const float* logprob, const float* mu, int64_t T, double* d3,
                      double* part, hipStream_t s);
+// The exact entries of a chunk (rz_exact.hip): the records of each token's
+// dominant probabilities, from the tile partials pm, lse, the target logit
+// zt, coef, the shift table and row factor, the stored e, hhat and W.
+hipError_t launch_select(const float* pm, int64_t TC, int V, const float* lse, const float* zt,
+                         const int32_t* target, const float* coef, const uint32_t* D, int64_t ds,
+                         const float* g, const uint16_t* E, const uint16_t* hh, const uint16_t* W,
+                         int H, SelRec* rec, hipStream_t s);
+// dhhat_t -= coef_t sum_records beta W[v] (before the RMSNorm backward).
+hipError_t launch_dh_fix(const SelRec* rec, const float* coef, const uint16_t* W, int64_t TC,
+                         int H, float* dh, hipStream_t s);
+// dW[v] += the one-hot terms and the records' exact terms, per row in token
+// order (after the chunk's weight-gradient contraction).
+hipError_t launch_dw_exact(const int32_t* target, const float* coef, const float* g,
+                           const SelRec* rec, const uint16_t* hh, int64_t TC, int H, int V,
+                           const DwExactBufs& wb, float* dW, hipStream_t s);
 hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64_t ds,
                                     const float* g, const float* coef_chunk,
                                     const int32_t* target_chunk, const uint16_t* hh,
                                     const uint16_t* x_chunk, float eps, const float* dhh_chunk,
                                     int64_t TC, int H, int V, int64_t gb0, int first,
-                                    uint16_t* hs, int32_t* ibuf, double* gpart, float* dW,
-                                    hipStream_t s);
+                                    uint16_t* hs, const SelRec* rec, const DwExactBufs& wb,
+                                    double* rbuf, double* gpart, float* dW, hipStream_t s);
 hipError_t launch_dgamma_final(const double* gpart, int64_t nb, int H, float* dgamma,
                                hipStream_t s);
 hipError_t launch_kl(const float* logprob, const float* mu, int64_t T, double* kl,

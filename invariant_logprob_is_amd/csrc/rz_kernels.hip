@@ -5,19 +5,9 @@
 
 #include "rz_gemm.h"
 #include "rz_gemm_tr.h"
+#include "rz_util.h"
 
 namespace rz {
-
-constexpr float kLog2e = 1.4426950408889634f;
-constexpr double kLn2 = 0.69314718055994530942;
-
-// The integer log2 reference of a vocabulary tile with max logit M: stored
-// values are e = 2^(z log2 e - m), 1/2 < max e <= 1.
-__device__ __forceinline__ float tile_ref(float M) { return ceilf(M * kLog2e); }
-
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float(uint32_t(b) << 16);
-}
 
 // float64 -> bf16, round to nearest even, with a single rounding: round to
 // odd at float32 precision (24 bits, >= 8 + 2) and then to nearest even at
@@ -47,16 +37,6 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   v[0] = static_cast<__bf16>(lo);
   v[1] = static_cast<__bf16>(hi);
   return __builtin_bit_cast(uint32_t, v);
-}
-
-// Sum over a 64-lane wavefront by xor butterfly.  At every level the two
-// partners add the same two values (a + b and b + a), so all lanes finish with
-// identical bits, and the tree does not depend on where the row sits in the
-// batch.
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = v + __shfl_xor(v, m, 64);
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -754,15 +734,44 @@ __device__ void response_advantage(const int64_t* __restrict__ ro, int R,
   }
 }
 
+// The ragged structure, checked once on the device: *ok = 1 iff resp_offsets
+// run from 0 to T and strictly increase, and group_offsets run from 0 to R
+// and strictly increase.  The kernels below read *ok; with a malformed
+// structure they write NaN to every token (coef, the token scale), every
+// advantage and the loss, and read no offset beyond its array.
+__global__ __launch_bounds__(256) void k_check_structure(const int64_t* __restrict__ ro, int R,
+                                                         const int64_t* __restrict__ go, int G,
+                                                         int64_t T, int* __restrict__ ok) {
+  int bad = 0;
+  if (threadIdx.x == 0) bad = (ro[0] != 0 || ro[R] != T || go[0] != 0 || go[G] != R) ? 1 : 0;
+  for (int i = threadIdx.x; i < R; i += 256) bad |= ro[i] >= ro[i + 1] ? 1 : 0;
+  for (int i = threadIdx.x; i < G; i += 256) bad |= go[i] >= go[i + 1] ? 1 : 0;
+  bad = __syncthreads_or(bad);
+  if (threadIdx.x == 0) *ok = bad ? 0 : 1;
+}
+
+// NaN into every one of the T entries of out, spread over the R workgroups
+// of a per-response kernel (malformed structure).
+template <class F>
+__device__ __forceinline__ void fill_nan_tokens(F* __restrict__ out, int64_t T, int R) {
+  for (int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x; t < T; t += int64_t(R) * 256)
+    out[t] = F(NAN);
+}
+
 // cs[t] = -A_i / (R L_i) for every token t of response i (float64): the
 // factor that turns w_t into d loss / d logprob_t.  One workgroup per
-// response; malformed structure -> NaN for that response's tokens.
+// response; a malformed structure gives NaN for every token.
 __global__ __launch_bounds__(256) void k_token_scale(const int64_t* __restrict__ ro, int R,
                                                      const int64_t* __restrict__ go, int G,
                                                      const float* __restrict__ reward, int64_t T,
+                                                     const int* __restrict__ okp,
                                                      double* __restrict__ cs) {
   __shared__ double sA;
   __shared__ int sok;
+  if (!*okp) {
+    fill_nan_tokens(cs, T, R);
+    return;
+  }
   const int i = blockIdx.x;
   if (threadIdx.x == 0) {
     double A;
@@ -816,6 +825,7 @@ __global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logpr
                                                  const int64_t* __restrict__ ro, int R,
                                                  const int64_t* __restrict__ go, int G,
                                                  const float* __restrict__ reward,
+                                                 const int* __restrict__ okp,
                                                  float* __restrict__ coef, float* __restrict__ adv,
                                                  double* __restrict__ part) {
   __shared__ double sh[256];
@@ -823,6 +833,14 @@ __global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logpr
   __shared__ int sok;
   const int i = blockIdx.x;
   const int tid = threadIdx.x;
+  if (!*okp) {
+    if (coef) fill_nan_tokens(coef, T, R);
+    if (tid == 0) {
+      part[i] = NAN;
+      if (adv) adv[i] = NAN;
+    }
+    return;
+  }
   const int64_t a = ro[i];
   const int64_t b = ro[i + 1];
   if (tid == 0) {
@@ -852,17 +870,13 @@ __global__ __launch_bounds__(256) void k_is_resp(const float* __restrict__ logpr
 }
 
 __global__ __launch_bounds__(256) void k_is_final(const double* __restrict__ part, int R,
-                                                  const int64_t* __restrict__ ro,
-                                                  const int64_t* __restrict__ go, int G,
-                                                  int64_t T, double* __restrict__ loss) {
+                                                  const int* __restrict__ okp,
+                                                  double* __restrict__ loss) {
   __shared__ double sh[256];
   double s = 0.0;
   for (int i = threadIdx.x; i < R; i += 256) s += part[i];
   s = block_sum_256(s, sh);
-  if (threadIdx.x == 0) {
-    const bool ok = ro[0] == 0 && ro[R] == T && go[0] == 0 && go[G] == R;
-    *loss = ok ? -s / double(R) : NAN;
-  }
+  if (threadIdx.x == 0) *loss = *okp ? -s / double(R) : NAN;
 }
 
 constexpr int64_t kD3Block = 16384;
@@ -986,8 +1000,9 @@ __global__ __launch_bounds__(256) void k_decompose_final(const double* __restric
 // of rz_gemm_tr.h reads e straight from the forward's fragment order with
 // transposing LDS reads and applies the exact exponent shift in registers.
 // Chunks add into dW in chunk order.
-// The one-hot part is added exactly in fp32, per target row in token order,
-// after a deterministic bucketing of the chunk's tokens by target.
+// The one-hot part, and the exact terms of each token's dominant
+// probabilities, are added in fp32 per vocabulary row in token order
+// (rz_exact.hip).
 // ---------------------------------------------------------------------------
 
 // hsT[h][t] = bf16(coef_t g_t hhat[t][h]) for the chunk's tokens t < TC
@@ -1010,7 +1025,7 @@ __global__ __launch_bounds__(256) void k_scale_rows_t(const uint16_t* __restrict
     uint16_t v = 0;
     if (t < TC) {
       const float x = __uint_as_float(uint32_t(hh[t * H + h0 + tx]) << 16);
-      v = __builtin_bit_cast(uint16_t, static_cast<__bf16>(x * (coef[t] * gf[t])));
+      v = scaled_hidden(x, coef[t], gf[t]);
     }
     tile[r][tx] = v;
   }
@@ -1052,126 +1067,6 @@ void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int
         }
       }
     }
-  }
-}
-
-__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
-  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i < n) p[i] = v;
-}
-
-// Tokens of a chunk per target row: count, then (k_scan_*) the bucket
-// offsets, then the tokens in each bucket (any order), then their order by
-// token index (rank = tokens of the bucket with a smaller index).
-__global__ __launch_bounds__(256) void k_bucket_count(const int32_t* __restrict__ target,
-                                                      int64_t TC, int V, int32_t* count) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= TC) return;
-  const int32_t v = target[t];
-  if (v >= 0 && v < V) atomicAdd(count + v, 1);
-}
-
-// Exclusive prefix sum of count[0..V) into off[0..V] (off[V] = total) in
-// three fixed-order phases over 1024-entry blocks: block totals, a scan of
-// the totals (one workgroup), then each block's scan from its base.
-__device__ __forceinline__ int32_t block_incl_scan_1024(int32_t v, int32_t* sh) {
-  const int tid = threadIdx.x;
-  sh[tid] = v;
-  __syncthreads();
-  for (int w = 1; w < 1024; w <<= 1) {
-    const int32_t add = tid >= w ? sh[tid - w] : 0;
-    __syncthreads();
-    sh[tid] += add;
-    __syncthreads();
-  }
-  return sh[tid];
-}
-
-__global__ __launch_bounds__(1024) void k_scan_blocks(const int32_t* __restrict__ count, int V,
-                                                      int32_t* __restrict__ btot) {
-  __shared__ int32_t sh[1024];
-  const int64_t i = int64_t(blockIdx.x) * 1024 + threadIdx.x;
-  const int32_t v = i < V ? count[i] : 0;
-  const int32_t inc = block_incl_scan_1024(v, sh);
-  if (threadIdx.x == 1023) btot[blockIdx.x] = inc;
-}
-
-__global__ __launch_bounds__(1024) void k_scan_totals(int32_t* __restrict__ btot, int nb) {
-  __shared__ int32_t sh[1024];
-  // nb <= 1024 * 1024 / 1024: one pass of up to 1024 totals per thread group
-  int32_t carry = 0;
-  for (int base = 0; base < nb; base += 1024) {
-    const int i = base + threadIdx.x;
-    const int32_t v = i < nb ? btot[i] : 0;
-    const int32_t inc = block_incl_scan_1024(v, sh);
-    __syncthreads();
-    if (i < nb) btot[i] = carry + inc - v;        // exclusive base of block i
-    carry += sh[1023];
-    __syncthreads();
-  }
-  if (threadIdx.x == 0) btot[nb] = carry;
-}
-
-__global__ __launch_bounds__(1024) void k_scan_apply(const int32_t* __restrict__ count, int V,
-                                                     const int32_t* __restrict__ btot, int nb,
-                                                     int32_t* __restrict__ off) {
-  __shared__ int32_t sh[1024];
-  const int64_t i = int64_t(blockIdx.x) * 1024 + threadIdx.x;
-  const int32_t v = i < V ? count[i] : 0;
-  const int32_t inc = block_incl_scan_1024(v, sh);
-  if (i < V) off[i] = btot[blockIdx.x] + inc - v;
-  if (blockIdx.x == 0 && threadIdx.x == 0) off[V] = btot[nb];
-}
-
-__global__ __launch_bounds__(256) void k_bucket_fill(const int32_t* __restrict__ target,
-                                                     int64_t TC, int V,
-                                                     const int32_t* __restrict__ off,
-                                                     int32_t* cursor, int32_t* __restrict__ slot) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= TC) return;
-  const int32_t v = target[t];
-  if (v >= 0 && v < V) slot[off[v] + atomicAdd(cursor + v, 1)] = int32_t(t);
-}
-
-__global__ __launch_bounds__(256) void k_bucket_order(const int32_t* __restrict__ target,
-                                                      int64_t TC, int V,
-                                                      const int32_t* __restrict__ off,
-                                                      const int32_t* __restrict__ count,
-                                                      const int32_t* __restrict__ slot,
-                                                      int32_t* __restrict__ sorted) {
-  const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (t >= TC) return;
-  const int32_t v = target[t];
-  if (v < 0 || v >= V) return;
-  const int32_t a = off[v], n = count[v];
-  int32_t rank = 0;
-  for (int32_t i = 0; i < n; ++i) rank += (slot[a + i] < int32_t(t)) ? 1 : 0;
-  sorted[a + rank] = int32_t(t);
-}
-
-// dW[v] += sum over the bucket of v, in token order, of coef_t hhat_t
-// (fp32).  One workgroup per bucket start: position i of the sorted order
-// starts a bucket when it is the first token of its target row.
-__global__ __launch_bounds__(256) void k_onehot_add(const int32_t* __restrict__ target,
-                                                    const int32_t* __restrict__ off,
-                                                    const int32_t* __restrict__ count, int V,
-                                                    const int32_t* __restrict__ sorted,
-                                                    const float* __restrict__ coef,
-                                                    const uint16_t* __restrict__ hh, int H,
-                                                    float* __restrict__ dW) {
-  const int32_t i = blockIdx.x;
-  if (i >= off[V]) return;                         // only tokens with a target in [0, V)
-  const int32_t t0 = sorted[i];
-  const int32_t v = target[t0];
-  if (off[v] != i) return;
-  const int32_t n = count[v];
-  for (int h = threadIdx.x; h < H; h += 256) {
-    float acc = 0.0f;
-    for (int32_t q = 0; q < n; ++q) {
-      const int32_t t = sorted[i + q];
-      acc = fmaf(coef[t], bf16_to_f32(hh[int64_t(t) * H + h]), acc);
-    }
-    dW[int64_t(v) * H + h] += acc;
   }
 }
 
@@ -1306,9 +1201,11 @@ hipError_t launch_shift_prep(const float* pm, const float* lse, int64_t T, int V
 }
 
 hipError_t launch_token_scale(const int64_t* ro, int R, const int64_t* go, int G,
-                              const float* reward, int64_t T, double* cs, hipStream_t s) {
+                              const float* reward, int64_t T, int* ok, double* cs,
+                              hipStream_t s) {
   ProfScope prof("k_token_scale", s);
-  hipLaunchKernelGGL(k_token_scale, dim3(R), dim3(256), 0, s, ro, R, go, G, reward, T, cs);
+  hipLaunchKernelGGL(k_check_structure, dim3(1), dim3(256), 0, s, ro, R, go, G, T, ok);
+  hipLaunchKernelGGL(k_token_scale, dim3(R), dim3(256), 0, s, ro, R, go, G, reward, T, ok, cs);
   return hipGetLastError();
 }
 
@@ -1343,11 +1240,14 @@ hipError_t launch_rmsnorm_bwd(const uint16_t* x, const uint16_t* gamma, float ep
 
 hipError_t launch_is_loss(const float* logprob, const float* mu, int64_t T, const int64_t* ro,
                           int R, const int64_t* go, int G, const float* reward, double* loss,
-                          float* coef, float* adv, double* part, hipStream_t s) {
+                          float* coef, float* adv, double* part, int* ok, bool check,
+                          hipStream_t s) {
   ProfScope prof("k_is_loss", s);
+  if (check)
+    hipLaunchKernelGGL(k_check_structure, dim3(1), dim3(256), 0, s, ro, R, go, G, T, ok);
   hipLaunchKernelGGL(k_is_resp, dim3(R), dim3(256), 0, s, logprob, mu, T, ro, R, go, G, reward,
-                     coef, adv, part);
-  hipLaunchKernelGGL(k_is_final, dim3(1), dim3(256), 0, s, part, R, ro, go, G, T, loss);
+                     ok, coef, adv, part);
+  hipLaunchKernelGGL(k_is_final, dim3(1), dim3(256), 0, s, part, R, ok, loss);
   return hipGetLastError();
 }
 
@@ -1365,19 +1265,10 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                                     const int32_t* target_chunk, const uint16_t* hh,
                                     const uint16_t* x_chunk, float eps, const float* dhh_chunk,
                                     int64_t TC, int H, int V, int64_t gb0, int first,
-                                    uint16_t* hs, int32_t* ibuf, double* gpart, float* dW,
-                                    hipStream_t s) {
+                                    uint16_t* hs, const SelRec* rec, const DwExactBufs& wb,
+                                    double* rbuf, double* gpart, float* dW, hipStream_t s) {
   const int64_t Vp = vocab_pad(V);
   const int64_t TCp = shift_stride(TC);
-  int32_t* count = ibuf;
-  int32_t* cursor = count + V;
-  int32_t* off = cursor + V;
-  int32_t* slot = off + V + 1;
-  int32_t* sorted = slot + TC;
-  int32_t* btot = sorted + TC;
-  double* rbuf = reinterpret_cast<double*>(
-      reinterpret_cast<char*>(ibuf) + align256(size_t(3 * int64_t(V) + 1 + 2 * TC +
-                                                      ceil_div(V, 1024) + 1) * 4));
   {
     ProfScope prof("k_dgamma_part", s);
     hipLaunchKernelGGL(k_row_rstd, dim3(blocks_for(TC, 4)), dim3(256), 0, s, x_chunk, eps, TC, H,
@@ -1396,24 +1287,10 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
     hipLaunchKernelGGL(k_dw_tr, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, E, D, ds,
                        hs, TCp, H, V, Vp, n_vt, n_ht, first, dW);
   }
-  {
-    ProfScope prof("k_onehot", s);
-    const int nbv = int(ceil_div(V, 1024));
-    hipLaunchKernelGGL(k_fill_i32, dim3(blocks_for(2 * int64_t(V), 256)), dim3(256), 0, s, count,
-                       2 * int64_t(V), 0);
-    hipLaunchKernelGGL(k_bucket_count, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
-                       TC, V, count);
-    hipLaunchKernelGGL(k_scan_blocks, dim3(nbv), dim3(1024), 0, s, count, V, btot);
-    hipLaunchKernelGGL(k_scan_totals, dim3(1), dim3(1024), 0, s, btot, nbv);
-    hipLaunchKernelGGL(k_scan_apply, dim3(nbv), dim3(1024), 0, s, count, V, btot, nbv, off);
-    hipLaunchKernelGGL(k_bucket_fill, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
-                       TC, V, off, cursor, slot);
-    hipLaunchKernelGGL(k_bucket_order, dim3(blocks_for(TC, 256)), dim3(256), 0, s, target_chunk,
-                       TC, V, off, count, slot, sorted);
-    hipLaunchKernelGGL(k_onehot_add, dim3(uint32_t(TC)), dim3(256), 0, s, target_chunk, off,
-                       count, V, sorted, coef_chunk, hh, H, dW);
-  }
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // the one-hot terms and the exact records, per row in token order
+  return launch_dw_exact(target_chunk, coef_chunk, g, rec, hh, TC, H, V, wb, dW, s);
 }
 
 hipError_t launch_dgamma_final(const double* gpart, int64_t nb, int H, float* dgamma,

@@ -279,6 +279,24 @@ def older_version(master: int, x_bits: np.ndarray, gamma_bits: np.ndarray, W_bit
     return moved(x_bits, x_sigma), moved(gamma_bits, gamma_sigma), moved(W_bits, w_sigma)
 
 
+def zipf_targets(master: int, T: int, V: int, exponent: float = 1.1, top_share: float = 0.3,
+                 chunk: int = 32768) -> np.ndarray:
+    """Target token ids with a Zipfian frequency profile, as natural text has:
+    id r (in a seeded random order of the vocabulary) is drawn with weight
+    (r + 1)^-exponent, and in every chunk of `chunk` consecutive tokens a
+    fraction top_share of the positions (a seeded random subset) holds the
+    most frequent id, as end-of-text or newline tokens do.  int32 [T]."""
+    rng = _rng(master, _C_TARGET)
+    order = rng.permutation(V)
+    w = (np.arange(V, dtype=np.float64) + 1.0) ** -exponent
+    t = order[rng.choice(V, size=T, p=w / w.sum())].astype(np.int32)
+    for c0 in range(0, T, chunk):
+        c1 = min(T, c0 + chunk)
+        k = rng.choice(c1 - c0, size=int(top_share * (c1 - c0)), replace=False)
+        t[c0 + k] = order[0]
+    return t
+
+
 CONFIGS = {
     "tiny": tiny,
     "qwen15b": qwen15b,
