@@ -384,50 +384,6 @@ def shards(args, b, rz, x, g, W, tgt, lp, lse, ws):
     }), flush=True)
 
 
-PROBE_MODES = {0: "zeros", 1: "random bf16 with the exponents of normal(0, 1) data",
-               2: "random bf16 with the magnitudes of LM-head weights and of e"}
-
-
-def run_mfma_peak(torch, rz):
-    """The register-only bf16 MFMA rate by operand data (rz_probe_mfma_peak),
-    with the shader clock sampled during each timed launch."""
-    import ctypes
-    grid, iters = 256, 2000000
-    flops = grid * 4 * 16 * 32768.0 * iters
-    out = torch.empty(grid * 256, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
-    L = rz.lib()
-    res = []
-    for rep in range(2):
-        for mode in PROBE_MODES:
-            st = L.rz_probe_mfma_peak(ctypes.c_void_p(out.data_ptr()), grid, 1000, mode,
-                                      ctypes.c_void_p(stream.cuda_stream))
-            if st != 0:
-                raise RuntimeError(f"rz_probe_mfma_peak failed ({st})")
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            with SclkSampler(0.02) as sclk:
-                e0.record(stream)
-                st = L.rz_probe_mfma_peak(ctypes.c_void_p(out.data_ptr()), grid, iters, mode,
-                                          ctypes.c_void_p(stream.cuda_stream))
-                e1.record(stream)
-                torch.cuda.synchronize()
-            if st != 0 or not bool(torch.isfinite(out).all()):
-                raise RuntimeError(f"rz_probe_mfma_peak mode {mode}: status {st} or non-finite output")
-            ms = e0.elapsed_time(e1)
-            tf = flops / (ms / 1000.0) / 1e12
-            r = {"mode": mode, "operands": PROBE_MODES[mode], "repeat": rep, "ms": ms,
-                 "tflops": tf, "frac_of_published_peak": tf * 1e12 / PEAK_BF16_FLOPS,
-                 "sclk": sclk.summary()}
-            log(f"mode {mode} ({PROBE_MODES[mode]}): {tf:.0f} TFLOP/s")
-            res.append(r)
-    print(json.dumps({
-        "metric": "register-only bf16 MFMA rate by operand data, 1 GPU", "unit": "TFLOP/s",
-        "n_gpus": 1, "peak": PEAK_BF16_FLOPS / 1e12,
-        "config": {"workload": f"{grid} blocks x 4 waves x 16 MFMA 32x32x16 x {iters} iterations"},
-        "results": res}), flush=True)
-
-
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -446,9 +402,6 @@ def main():
     ap.add_argument("--shards", type=int, choices=[1, 2, 4, 8],
                     help="time the log-probabilities through this many equal shares of the "
                          "vocabulary splits and their merge instead of the learner step")
-    ap.add_argument("--mfma-peak", action="store_true",
-                    help="measure the register-only bf16 MFMA rate for zero and random operands "
-                         "(rz_probe_mfma_peak) instead of the learner step")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
                          "into profiles/traffic_<kernel>.json and exit")
@@ -468,9 +421,6 @@ def main():
     import workloads
 
     rz.lib()
-    if args.mfma_peak:
-        run_mfma_peak(torch, rz)
-        return
     dev = torch.device("cuda", 0)
     t_gen = time.perf_counter()
     b = workloads.CONFIGS[args.config]()

@@ -399,22 +399,6 @@ RZ_API int rz_profile_enable(int on);
 RZ_API int rz_profile_count(void);
 RZ_API int rz_profile_get(int i, const char** name, double* total_ms, int64_t* launches);
 
-/*
- * rz_probe_mfma_peak -- the register-only bf16 MFMA rate of this GPU, for
- * benchmarks (not part of the method).  Launches `grid` blocks of 4 waves;
- * each wave multiplies register-resident 32x32x16 bf16 fragments into 16
- * independent fp32 accumulators, `iters` times: grid * 4 * 16 * 32768 * iters
- * flops.  The operands are built in registers: mode 0 zeros, mode 1 random
- * values with the exponents of normal(0, 1) data, mode 2 random values with
- * the magnitudes of LM-head weights and of the stored exponentials.  On a
- * power-limited chip the rate depends on the data.  Reads no memory; writes
- * the sum of each thread's accumulators to out[grid * 256] (fp32, caller-owned
- * device memory, 4-byte aligned).  Time it with events on `stream`.
- * Errors: RZ_EINVAL (null or misaligned out, grid outside [1, 65536], iters
- * outside [1, 1e8], mode outside 0..2), RZ_ENODEV, RZ_EHIP.
- */
-RZ_API int rz_probe_mfma_peak(float* out, int32_t grid, int32_t iters, int32_t mode, void* stream);
-
 #ifdef __cplusplus
 }  /* extern "C" */
 #endif

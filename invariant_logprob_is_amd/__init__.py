@@ -61,7 +61,6 @@ SYMBOLS = {
     "rz_logprob_shard": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _I32, _I32, _P,
                                         _P, _SZ, _P]),
     "rz_logprob_merge": (ctypes.c_int, [_P, _P, _I64, _I32, _P, _P, _P]),
-    "rz_probe_mfma_peak": (ctypes.c_int, [_P, _I32, _I32, _I32, _P]),
     "rz_profile_enable": (ctypes.c_int, [ctypes.c_int]),
     "rz_profile_count": (ctypes.c_int, []),
     "rz_profile_get": (ctypes.c_int, [ctypes.c_int, ctypes.POINTER(ctypes.c_char_p),

@@ -287,18 +287,8 @@ def test_shard_and_merge_argument_validation():
     assert L.rz_logprob_merge(FAKE, FAKE, 10, 4000001, FAKE, FAKE, None) == rz.RZ_EINVAL
 
 
-def test_mfma_probe_argument_validation():
-    f = rz.lib().rz_probe_mfma_peak
-    assert f(None, 256, 10, 1, None) == rz.RZ_EINVAL
-    assert f(FAKE + 2, 256, 10, 1, None) == rz.RZ_EINVAL
-    for grid, iters, mode in ((0, 10, 1), (65537, 10, 1), (256, 0, 1), (256, 100000001, 1),
-                              (256, 10, -1), (256, 10, 3)):
-        assert f(FAKE, grid, iters, mode, None) == rz.RZ_EINVAL, (grid, iters, mode)
-
-
 @pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
 def test_no_device_is_reported():
-    assert rz.lib().rz_probe_mfma_peak(FAKE, 256, 10, 1, None) == rz.RZ_ENODEV
     assert _rmsnorm() == rz.RZ_ENODEV
     assert _rmsnorm(rstd=None) == rz.RZ_ENODEV
     assert _logprob() == rz.RZ_ENODEV

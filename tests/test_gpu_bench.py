@@ -38,19 +38,3 @@ def test_bench_json_line(gpu):
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
     for k, v in d["side_kernels"].items():
         assert v["achieved_GBps"] > 0 and v["ms_per_step"] > 0, k
-
-
-def test_mfma_probe(gpu):
-    import ctypes
-    import torch
-    import invariant_logprob_is_amd as rz
-    L = rz.lib()
-    out = torch.full((256 * 256,), float("nan"), dtype=torch.float32, device=gpu)
-    stream = ctypes.c_void_p(torch.cuda.current_stream(gpu).cuda_stream)
-    for mode in (0, 1, 2):
-        assert L.rz_probe_mfma_peak(ctypes.c_void_p(out.data_ptr()), 256, 100, mode, stream) == 0
-        torch.cuda.synchronize()
-        o = out.cpu()
-        assert bool(torch.isfinite(o).all()), mode
-        if mode == 0:
-            assert bool((o == 0).all())
