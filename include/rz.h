@@ -148,6 +148,30 @@ RZ_API int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps,
                void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rz_logprob_noalloc -- rz_logprob for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation.  It takes no workspace and allocates nothing: its
+ * scratch is a built-in device array of RZ_NOALLOC_SCRATCH_BYTES that each
+ * GPU the library runs on holds until the process ends (its address is
+ * looked up on the first call on each device).  The results are those of
+ * rz_logprob, bit for bit (same kernels, same invariance).
+ *
+ * Limit: the call's scratch, the rz_logprob part of rz_workspace_bytes (the
+ * normalised rows and per-tile partials of one chunk of at most 32,768
+ * tokens), must fit: about 8,500 tokens at H = 1536 and V = 151,936; larger
+ * calls return RZ_EWORKSPACE before any HIP call.  Every call on a GPU uses
+ * that GPU's one array: calls that overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.
+ *
+ * Arguments and other errors as rz_logprob.
+ */
+#define RZ_NOALLOC_SCRATCH_BYTES (64u << 20)
+RZ_API int rz_logprob_noalloc(const uint16_t* x, const uint16_t* gamma, float eps,
+                              const uint16_t* W, const int32_t* target,
+                              int64_t T, int32_t H, int32_t V,
+                              float* logprob, float* lse, void* stream);
+
+/*
  * rz_is_loss -- unclipped token-level IS REINFORCE loss and its gradient.
  *
  * ([P2] "Alignment permits a simpler learning path": advantage = reward minus

@@ -20,7 +20,8 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "logprob", "is_loss", "d3", "kl",
+    "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "logprob",
+    "logprob_noalloc", "NOALLOC_SCRATCH_BYTES", "is_loss", "d3", "kl",
     "decompose", "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH",
     "VOCAB_SPLITS", "vocab_split_begin", "logprob_shard", "logprob_merge", "split_records",
     "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
@@ -48,6 +49,7 @@ SYMBOLS = {
     "rz_workspace_bytes_grads": (_SZ, [_I64, _I32, _I32]),
     "rz_rmsnorm": (ctypes.c_int, [_P, _P, _F32, _I64, _I32, _P, _P, _P]),
     "rz_logprob": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _SZ, _P]),
+    "rz_logprob_noalloc": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P]),
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_backward": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]),
@@ -195,6 +197,35 @@ def logprob(x, gamma, W, target, eps: float = 1e-6, *, workspace=None, out=None,
                           target.data_ptr(), T, H, V, lp.data_ptr(), ls.data_ptr(),
                           ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_logprob", st)
+    return lp, ls
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # RZ_NOALLOC_SCRATCH_BYTES
+
+
+def logprob_noalloc(x, gamma, W, target, eps: float = 1e-6, *, out=None, lse_out=None):
+    """rz_logprob_noalloc: logprob() on the library's built-in device scratch,
+    with no workspace (same bits as logprob()).  For callers that cannot
+    allocate, pass preallocated `out` and `lse_out`.  Calls that overlap on
+    one GPU race on the scratch.  Returns (logprob [T] fp32, lse [T] fp32)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    V = W.shape[0]
+    if gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T:
+        raise ValueError("shape mismatch among x, gamma, W, target")
+    lp = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    ls = lse_out if lse_out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    _need(lp, "out", torch.float32, dev, 1)
+    _need(ls, "lse_out", torch.float32, dev, 1)
+    st = lib().rz_logprob_noalloc(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                                  target.data_ptr(), T, H, V, lp.data_ptr(), ls.data_ptr(),
+                                  _stream(dev))
+    _check("rz_logprob_noalloc", st)
     return lp, ls
 
 

@@ -1,5 +1,8 @@
 // C ABI of the learner head (declared in include/rz.h).  Every check that
 // needs no device data runs before the first HIP call.
+#include <atomic>
+#include <mutex>
+
 #include "rz.h"
 #include "rz_internal.h"
 
@@ -84,6 +87,42 @@ hipError_t run_shard(const uint16_t* x, const uint16_t* gamma, float eps, const 
   return e;
 }
 
+// ---------------------------------------------------------------------------
+// Scratch of rz_logprob_noalloc: a file-scope device array, which every GPU
+// the library runs on holds until the process ends.  In host code its name
+// is only a stand-in; the device address is looked up once per device with
+// hipGetSymbolAddress, with that device current, and that address is what
+// the kernels get.  Nothing in it has to start at zero: the forward writes
+// every partial it later reads, and the target logits are filled by a
+// kernel before the forward.
+// ---------------------------------------------------------------------------
+static_assert(RZ_NOALLOC_SCRATCH_BYTES % 256 == 0, "scratch size");
+static __device__ __align__(256) char scratch[RZ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The device address of `scratch` on the current device.
+hipError_t scratch_on_current_device(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess || !p) return e != hipSuccess ? e : hipErrorInvalidSymbol;
+      g_scratch[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return hipSuccess;
+}
+
 }  // namespace
 
 extern "C" {
@@ -129,6 +168,27 @@ int rz_logprob(const uint16_t* x, const uint16_t* gamma, float eps, const uint16
   if (st != RZ_OK) return st;
 
   return status_of(run_logprob(x, gamma, eps, W, target, T, H, V, logprob, lse, workspace, L,
+                               static_cast<hipStream_t>(stream)));
+}
+
+int rz_logprob_noalloc(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                       const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
+                       float* lse, void* stream) {
+  if (!x || !gamma || !W || !target || !logprob) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) ||
+      !aligned4(logprob) || (lse && !aligned4(lse)))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  const WsLayout L = ws_layout(T, H, V);
+  if (L.fwd_end > size_t(RZ_NOALLOC_SCRATCH_BYTES)) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  void* ws = nullptr;
+  if (scratch_on_current_device(&ws) != hipSuccess) return RZ_EHIP;
+  // the same launches as rz_logprob, on the built-in scratch
+  return status_of(run_logprob(x, gamma, eps, W, target, T, H, V, logprob, lse, ws, L,
                                static_cast<hipStream_t>(stream)));
 }
 

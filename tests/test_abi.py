@@ -287,8 +287,38 @@ def test_shard_and_merge_argument_validation():
     assert L.rz_logprob_merge(FAKE, FAKE, 10, 4000001, FAKE, FAKE, None) == rz.RZ_EINVAL
 
 
+def test_noalloc_argument_validation():
+    f = rz.lib().rz_logprob_noalloc
+    ok = (FAKE, FAKE, 1e-6, FAKE, FAKE, 10, 128, 1024, FAKE, FAKE, None)
+
+    def call(**kw):
+        a = list(ok)
+        names = ["x", "gamma", "eps", "W", "target", "T", "H", "V", "logprob", "lse", "stream"]
+        for k, v in kw.items():
+            a[names.index(k)] = v
+        return f(*a)
+
+    for k in ("x", "gamma", "W", "target", "logprob"):
+        assert call(**{k: None}) == rz.RZ_EINVAL, k
+    assert call(x=FAKE + 8) == rz.RZ_EINVAL
+    assert call(target=FAKE + 2) == rz.RZ_EINVAL
+    assert call(eps=-1.0) == rz.RZ_EINVAL
+    assert call(T=0) == rz.RZ_EINVAL
+    assert call(H=100) == rz.RZ_EUNSUPPORTED
+    # beyond the built-in scratch (8,572 rows at the 1.5B-shaped head):
+    # rejected on the host, before any HIP call
+    assert call(T=8573, H=1536, V=151936) == rz.RZ_EWORKSPACE
+    assert call(T=4096, H=16384, V=1024) == rz.RZ_EWORKSPACE
+    # the path runs in chunks of 32,768 rows: a long batch on a small head fits
+    if not _gpu_present():
+        assert call(T=1 << 20, H=128, V=1024) == rz.RZ_ENODEV
+    assert rz.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
 @pytest.mark.skipif(_gpu_present(), reason="valid arguments would reach the GPU")
 def test_no_device_is_reported():
+    assert rz.lib().rz_logprob_noalloc(FAKE, FAKE, 1e-6, FAKE, FAKE, 8572, 1536, 151936, FAKE,
+                                       FAKE, None) == rz.RZ_ENODEV
     assert _rmsnorm() == rz.RZ_ENODEV
     assert _rmsnorm(rstd=None) == rz.RZ_ENODEV
     assert _logprob() == rz.RZ_ENODEV
