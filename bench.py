@@ -65,28 +65,51 @@ def measured_traffic(kernel: str):
     return d.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name, from /proc/cpuinfo (or the platform)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or platform.machine()
+
+
 def cpu_baseline(b, n_tokens: int):
     """The oracle as it stands, on the first `n_tokens` rows of the batch
-    (whole responses are not needed: rows are independent in the head)."""
+    (whole responses are not needed: rows are independent in the head), with
+    the BLAS thread pools set to every core this process may run on."""
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        from threadpoolctl import threadpool_info, threadpool_limits
+        limiter = threadpool_limits(limits=cores)
     except Exception:  # pragma: no cover
-        threads = len(os.sched_getaffinity(0))
-    n = min(n_tokens, b.T)
-    rows = slice(0, n)
-    mu_noise = b.lag_noise[rows].astype(np.float64)
-    t0 = time.perf_counter()
-    lp, lse = oracle.logprob(b.x[rows], b.gamma, b.eps, b.W, b.target[rows])
-    mu = lp + mu_noise
-    ro = np.array([0, n], np.int64)
-    go = np.array([0, 1], np.int64)
-    L = oracle.is_loss(lp, mu, ro, go, b.reward[:1])
-    oracle.d3(lp, mu)
-    oracle.backward(b.x[rows], b.gamma, b.eps, b.W, b.target[rows], lse, L["coef"])
-    dt = time.perf_counter() - t0
+        threadpool_info, limiter = None, None
+    try:
+        threads = cores
+        if threadpool_info is not None:
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        n = min(n_tokens, b.T)
+        rows = slice(0, n)
+        mu_noise = b.lag_noise[rows].astype(np.float64)
+        t0 = time.perf_counter()
+        lp, lse = oracle.logprob(b.x[rows], b.gamma, b.eps, b.W, b.target[rows])
+        mu = lp + mu_noise
+        ro = np.array([0, n], np.int64)
+        go = np.array([0, 1], np.int64)
+        L = oracle.is_loss(lp, mu, ro, go, b.reward[:1])
+        oracle.d3(lp, mu)
+        oracle.backward(b.x[rows], b.gamma, b.eps, b.W, b.target[rows], lse, L["coef"])
+        dt = time.perf_counter() - t0
+    finally:
+        if limiter is not None:
+            limiter.restore_original_limits()
     return {"value": n / dt, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model(), "affinity_cores": cores,
             "sample": f"first {n} rows of the workload: RMSNorm, LM head, log-softmax, IS loss, "
                       f"D3 and backward to the hidden states in float64 numpy ({dt:.1f} s)"}
 

@@ -28,7 +28,10 @@ __all__ = [
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
 ]
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librz.so")
+# RZ_LIB_PATH selects another build of the same library (the sanitized
+# librz_san.so of the CPU tests); there is no fallback of any kind.
+LIB_PATH = os.environ.get("RZ_LIB_PATH") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "librz.so")
 
 RZ_OK, RZ_EINVAL, RZ_EUNSUPPORTED, RZ_ENODEV, RZ_EHIP, RZ_EWORKSPACE = range(6)
 

@@ -1,9 +1,14 @@
 """Build librz.so (the HIP library behind include/rz.h) in-tree for gfx950.
 
-    python -m invariant_logprob_is_amd.build
+    python -m invariant_logprob_is_amd.build [--sanitize]
 
 compiles every csrc/*.hip with hipcc and links them into
 invariant_logprob_is_amd/librz.so.  Always recompiles.
+
+--sanitize builds librz_san.so instead: the same sources with the host code
+instrumented by AddressSanitizer and UndefinedBehaviorSanitizer (the device
+code is unchanged).  The CPU test tests/test_sanitized_abi.py runs the C-ABI
+tests against it with the sanitizer runtime loaded.
 """
 from __future__ import annotations
 
@@ -19,6 +24,10 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "librz.so")
+SAN_LIB = os.path.join(PKG, "librz_san.so")
+# host-only sanitizer flags: each -fsanitize= goes to the host compilation
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-omit-frame-pointer", "-Xarch_host", "-fno-sanitize-recover=all"]
 
 ARCH = "gfx950"
 CFLAGS = [
@@ -48,27 +57,37 @@ def _run(cmd):
     return out
 
 
-def build(verbose: bool = False) -> str:
+def sanitizer_runtime() -> str:
+    """Path of the AddressSanitizer runtime that hipcc's clang links against
+    (it carries the UndefinedBehaviorSanitizer handlers too)."""
+    return _run([_hipcc(), "-print-file-name=libclang_rt.asan-x86_64.so"]).strip()
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
+    bdir = os.path.join(BUILD_DIR, "san") if sanitize else BUILD_DIR
+    lib = SAN_LIB if sanitize else LIB
+    extra = SAN_FLAGS if sanitize else []
+    os.makedirs(bdir, exist_ok=True)
     srcs = sorted(f for f in os.listdir(CSRC) if f.endswith(".hip"))
-    objs = [os.path.join(BUILD_DIR, s[:-4] + ".o") for s in srcs]
+    objs = [os.path.join(bdir, s[:-4] + ".o") for s in srcs]
 
     def compile_one(i):
-        return _run([hipcc, *CFLAGS, "-c", os.path.join(CSRC, srcs[i]), "-o", objs[i]])
+        return _run([hipcc, *CFLAGS, *extra, "-c", os.path.join(CSRC, srcs[i]), "-o", objs[i]])
 
     with ThreadPoolExecutor(max_workers=min(4, len(srcs))) as ex:
         outs = list(ex.map(compile_one, range(len(srcs))))
-    tmp = LIB + ".tmp"
-    outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]))
-    os.replace(tmp, LIB)
+    tmp = lib + ".tmp"
+    outs.append(_run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *extra, *objs, "-o",
+                      tmp]))
+    os.replace(tmp, lib)
     if verbose:
         for o in outs:
             if o.strip():
                 print(o)
-        print(f"built {LIB}")
-    return LIB
+        print(f"built {lib}")
+    return lib
 
 
 if __name__ == "__main__":
-    build(verbose="-q" not in sys.argv)
+    build(verbose="-q" not in sys.argv, sanitize="--sanitize" in sys.argv)

@@ -36,5 +36,6 @@ def test_bench_json_line(gpu):
     assert abs(r["frac"] - r["achieved"] / r["peak"]) <= 1e-9
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["value"] > 0 and cb["cores"] >= 1
+    assert cb["cpu_model"] and cb["affinity_cores"] >= 1
     for k, v in d["side_kernels"].items():
         assert v["achieved_GBps"] > 0 and v["ms_per_step"] > 0, k
