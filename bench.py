@@ -196,14 +196,18 @@ class SclkSampler:
                 "samples": int(v.size), "source": self.path}
 
 
-def summarize_counters(fetch_csv: str, write_csv: str):
-    """Per-launch HBM traffic of the head's kernels from rocprofv3 counter
+def summarize_counters(fetch_csv: str, write_csv: str, dram_csv: str = None):
+    """Per-launch memory traffic of the head's kernels from rocprofv3 counter
     collection (FETCH_SIZE and WRITE_SIZE are in KiB per dispatch), scaled by
-    what the same counters read for the calibration copy of known size."""
+    what the same counters read for the calibration copy of known size.
+    With dram_csv, a third pass of TCC_EA0_RDREQ_DRAM_sum and
+    TCC_EA0_WRREQ_DRAM_sum (the L2's read and write requests to local memory,
+    counted in requests) is turned into bytes with the same copy's
+    requests per byte."""
     import csv
     import collections
 
-    def per_kernel(path, counter):
+    def per_kernel(path, counter, unit=1024.0):
         acc = collections.defaultdict(list)
         for r in csv.DictReader(open(path)):
             if r["Counter_Name"] != counter:
@@ -212,7 +216,7 @@ def summarize_counters(fetch_csv: str, write_csv: str):
             acc[(name, r["Dispatch_Id"])].append(float(r["Counter_Value"]))
         out = collections.defaultdict(list)
         for (name, _), v in acc.items():
-            out[name].append(sum(v) * 1024.0)
+            out[name].append(sum(v) * unit)
         return out
 
     fetch = per_kernel(fetch_csv, "FETCH_SIZE")
@@ -220,6 +224,12 @@ def summarize_counters(fetch_csv: str, write_csv: str):
     copy = "__amd_rocclr_copyBuffer"
     cf = max(fetch.get(copy, [0.0])) / CALIBRATION_BYTES
     cw = max(write.get(copy, [0.0])) / CALIBRATION_BYTES
+    dram = None
+    if dram_csv:
+        drd = per_kernel(dram_csv, "TCC_EA0_RDREQ_DRAM_sum", 1.0)
+        dwr = per_kernel(dram_csv, "TCC_EA0_WRREQ_DRAM_sum", 1.0)
+        dram = (drd, dwr, max(drd.get(copy, [0.0])) / CALIBRATION_BYTES,
+                max(dwr.get(copy, [0.0])) / CALIBRATION_BYTES)
     os.makedirs(PROFILES, exist_ok=True)
     sha = source_sha()
     # the learner step launches the storing forward variant; k_dw (--grads)
@@ -237,10 +247,23 @@ def summarize_counters(fetch_csv: str, write_csv: str):
                  "copy_bytes": CALIBRATION_BYTES, "fetch_factor": cf, "write_factor": cw},
              "source": "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE of bench.py, KiB per dispatch, "
                        "divided by the factor the same counter reads for a copy of copy_bytes"}
+        if dram is not None and all(x in dram[0] and x in dram[1] for x in disps):
+            drd, dwr, crd, cwr = dram
+            d["dram_read_bytes_per_launch"] = sum(float(np.mean(drd[x])) for x in disps) / (crd or 1.0)
+            d["dram_write_bytes_per_launch"] = sum(float(np.mean(dwr[x])) for x in disps) / (cwr or 1.0)
+            d["calibration"]["dram_read_requests_per_byte"] = crd
+            d["calibration"]["dram_write_requests_per_byte"] = cwr
+            d["dram_source"] = ("rocprofv3 --pmc TCC_EA0_RDREQ_DRAM_sum TCC_EA0_WRREQ_DRAM_sum: the L2's "
+                                "requests to local memory (the MALL serves some of them; no counter "
+                                "on this part separates MALL hits from HBM), divided by the requests "
+                                "per byte of the same copy")
         with open(os.path.join(PROFILES, f"traffic_{k}.json"), "w") as fh:
             json.dump(d, fh, indent=1)
         print(f"{k}: {f / 1e9:.3f} GB fetched + {w / 1e9:.3f} GB written per launch "
-              f"(factors {cf:.3f}, {cw:.3f})")
+              f"(factors {cf:.3f}, {cw:.3f})"
+              + (f"; local-memory requests {d['dram_read_bytes_per_launch'] / 1e9:.3f} GB read, "
+                 f"{d['dram_write_bytes_per_launch'] / 1e9:.3f} GB written"
+                 if "dram_read_bytes_per_launch" in d else ""))
 
 
 def probe(args, b, rz, x, g, W, tgt, lp, ws, stream):
@@ -425,13 +448,16 @@ def main():
     ap.add_argument("--shards", type=int, choices=[1, 2, 4, 8],
                     help="time the log-probabilities through this many equal shares of the "
                          "vocabulary splits and their merge instead of the learner step")
-    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="turn two rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE) "
-                         "into profiles/traffic_<kernel>.json and exit")
+    ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
+                    help="turn rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE and "
+                         "optionally TCC_EA0_RDREQ_DRAM_sum + TCC_EA0_WRREQ_DRAM_sum) into "
+                         "profiles/traffic_<kernel>.json and exit")
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0 or args.cpu_tokens < 1:
         ap.error("--steps and --cpu-tokens must be at least 1, --warmup at least 0")
     if args.summarize_counters:
+        if len(args.summarize_counters) not in (2, 3):
+            ap.error("--summarize-counters takes FETCH_CSV WRITE_CSV [DRAM_CSV]")
         summarize_counters(*args.summarize_counters)
         return
     if args.gpus != 1:

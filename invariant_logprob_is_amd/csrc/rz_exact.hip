@@ -361,7 +361,7 @@ __global__ __launch_bounds__(256) void k_dw_keys(const int32_t* __restrict__ tar
   }
 }
 
-constexpr int kRsRounds = 8;                    // rounds of 256 keys per block
+constexpr int kRsRounds = 16;                   // rounds of 256 keys per block
 constexpr int kRsItems = 256 * kRsRounds;
 static_assert(kRsItems == kRsItemsPerBlock, "sort block size");
 static_assert(kEnt == kEntPerToken, "entries per token");
@@ -384,15 +384,25 @@ __global__ __launch_bounds__(256) void k_rs_hist(const int32_t* __restrict__ key
   hist[int64_t(threadIdx.x) * nblk + blockIdx.x] = cnt[threadIdx.x];
 }
 
-// Exclusive prefix sum of a[0..n) in place, one block: each thread sums a
-// contiguous run, the run totals are scanned, each run is rewritten.
+// Exclusive prefix sum of a[0..n) in place, one block, n <= kScanMax: the
+// array is copied into LDS with coalesced loads, each thread sums a
+// contiguous run there, the run totals are scanned, each run is rewritten,
+// and the result is copied back.
+constexpr int kScanMax = 33 * 1024;
+static_assert(kBwdChunk + 1 <= kScanMax, "per-token offsets fit the scan");
+static_assert(256 * ((kBwdChunk * kEnt + kRsItems - 1) / kRsItems) <= kScanMax,
+              "digit counts fit the scan");
+
 __global__ __launch_bounds__(1024) void k_rs_scan(int32_t* __restrict__ a, int64_t n) {
+  __shared__ int32_t buf[kScanMax];
   __shared__ int32_t sh[1024];
   const int tid = threadIdx.x;
+  for (int64_t i = tid; i < n; i += 1024) buf[i] = a[i];
+  __syncthreads();
   const int64_t per = (n + 1023) / 1024;
   const int64_t b = tid * per, e = b + per < n ? b + per : n;
   int32_t s = 0;
-  for (int64_t i = b; i < e; ++i) s += a[i];
+  for (int64_t i = b; i < e; ++i) s += buf[i];
   sh[tid] = s;
   __syncthreads();
   for (int w = 1; w < 1024; w <<= 1) {
@@ -403,10 +413,12 @@ __global__ __launch_bounds__(1024) void k_rs_scan(int32_t* __restrict__ a, int64
   }
   int32_t run = sh[tid] - s;
   for (int64_t i = b; i < e; ++i) {
-    const int32_t v = a[i];
-    a[i] = run;
+    const int32_t v = buf[i];
+    buf[i] = run;
     run += v;
   }
+  __syncthreads();
+  for (int64_t i = tid; i < n; i += 1024) a[i] = buf[i];
 }
 
 // Stable scatter by digit: within a round of 256 keys, a key's rank among

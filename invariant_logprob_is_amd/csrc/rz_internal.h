@@ -65,7 +65,7 @@ inline int64_t shift_stride(int64_t tc) { return round_up(tc, kTile); }
 // kRsItemsPerBlock keys per block; the partial sums of buckets that span
 // blocks of 64 sorted positions, two per block.
 constexpr int kEntPerToken = kSelSlots + 1;
-constexpr int kRsItemsPerBlock = 2048;
+constexpr int kRsItemsPerBlock = 4096;
 struct DwExactBufs {
   int32_t* keys[2];
   int32_t* vals[2];

@@ -1109,14 +1109,37 @@ __global__ __launch_bounds__(256) void k_dgamma_part(const float* __restrict__ d
   part[(gb0 + blockIdx.x) * H + k] = s;
 }
 
-__global__ __launch_bounds__(256) void k_dgamma_final(const double* __restrict__ part,
-                                                      int64_t nb, int H,
-                                                      float* __restrict__ dgamma) {
-  const int k = blockIdx.x * 256 + threadIdx.x;
-  if (k >= H) return;
+// dgamma[k] = the sum of the row-block partials part[b][k] in block order,
+// cut into 16 contiguous ranges of blocks (a function of nb alone): each of
+// 16 waves sums one range in order for 64 columns, and the 16 range sums are
+// added in range order.  Loads run 8 blocks ahead of the sum.
+__global__ __launch_bounds__(1024) void k_dgamma_final(const double* __restrict__ part,
+                                                       int64_t nb, int H,
+                                                       float* __restrict__ dgamma) {
+  __shared__ double rs[16][64];
+  const int c = threadIdx.x & 63;
+  const int r = threadIdx.x >> 6;
+  const int k = blockIdx.x * 64 + c;
   double s = 0.0;
-  for (int64_t b = 0; b < nb; ++b) s += part[b * H + k];
-  dgamma[k] = float(s);
+  if (k < H) {
+    const int64_t b0 = nb * r / 16, b1 = nb * (r + 1) / 16;
+    int64_t b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      double v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(b + u) * H + k];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += part[b * H + k];
+  }
+  rs[r][c] = s;
+  __syncthreads();
+  if (r == 0 && k < H) {
+    double t = 0.0;
+    for (int q = 0; q < 16; ++q) t += rs[q][c];
+    dgamma[k] = float(t);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1296,7 +1319,7 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
 hipError_t launch_dgamma_final(const double* gpart, int64_t nb, int H, float* dgamma,
                                hipStream_t s) {
   ProfScope prof("k_dgamma_part", s);
-  hipLaunchKernelGGL(k_dgamma_final, dim3(blocks_for(H, 256)), dim3(256), 0, s, gpart, nb, H,
+  hipLaunchKernelGGL(k_dgamma_final, dim3(blocks_for(H, 64)), dim3(1024), 0, s, gpart, nb, H,
                      dgamma);
   return hipGetLastError();
 }
