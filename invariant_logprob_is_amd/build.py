@@ -36,6 +36,9 @@ CFLAGS = [
     "-fvisibility=hidden",
     # keep the compiler from forming packed fp32 math on its own
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # an atomic add by one lane stays one plain atomic: the wave-level
+    # rewrite would read its result back at once and stall on it
+    "-mllvm", "-amdgpu-atomic-optimizer-strategy=None",
     "-Wall", "-Wno-unused-function",
     f"-I{INCLUDE}", f"-I{CSRC}",
 ]

@@ -50,12 +50,13 @@ hipError_t run_logprob(const uint16_t* x, const uint16_t* gamma, float eps, cons
   float* pm = at<float>(workspace, L.pm);
   float* ps = at<float>(workspace, L.ps);
   float* zt = at<float>(workspace, L.ztgt);
+  int* tick = at<int>(workspace, L.tick);
   hipError_t e = hipSuccess;
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, nullptr, s);
     if (e == hipSuccess)
-      e = launch_lmhead_fwd(hhat, W, target + c0, tc, H, V, pm, ps, zt, nullptr, s);
+      e = launch_lmhead_fwd(hhat, W, target + c0, tc, H, V, pm, ps, zt, nullptr, tick, s);
     if (e == hipSuccess)
       e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse ? lse + c0 : nullptr, nullptr,
                              nullptr, nullptr, nullptr, 0, nullptr, s);
@@ -79,7 +80,8 @@ hipError_t run_shard(const uint16_t* x, const uint16_t* gamma, float eps, const 
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, nullptr, s);
     if (e == hipSuccess)
-      e = launch_lmhead_fwd_range(hhat, W, target + c0, tc, H, v0, Vs, pm, ps, zt, s);
+      e = launch_lmhead_fwd_range(hhat, W, target + c0, tc, H, v0, Vs, pm, ps, zt,
+                                  at<int>(workspace, L.tick), s);
     if (e == hipSuccess)
       e = launch_split_partials(pm, ps, zt, target + c0, tc, V, s0, s1,
                                 static_cast<char*>(partials) + c0 * sizeof(rz_vocab_split), T, s);
@@ -376,7 +378,9 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     const int64_t ds = shift_stride(tc);
     e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
-    if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
+    if (e == hipSuccess)
+      e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E,
+                            at<int>(workspace, L.b_tick), s);
     if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
     if (e == hipSuccess)
       e = launch_select(pm, tc, V, lse + c0, zt, target + c0, coef + c0, D, ds, g, E, hh, W, H,
@@ -440,7 +444,9 @@ int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const u
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
     const int64_t ds = shift_stride(tc);
     e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
-    if (e == hipSuccess) e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E, s);
+    if (e == hipSuccess)
+      e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E,
+                            at<int>(workspace, L.s_tick), s);
     if (e == hipSuccess)
       e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse_ + c0, cs + c0,
                              rollout_logprob + c0, coef_ + c0, D, ds, g, s);

@@ -173,8 +173,14 @@ struct GemmCoreT {
   __device__ __forceinline__ static int wave_m(int w) { return w % kWA; }
   __device__ __forceinline__ static int wave_n(int w) { return w / kWA; }
   __amdgpu_buffer_rsrc_t ra, rb;
-  uint32_t va[8];            // per-lane byte offsets of the load instructions (B, and A if
-                             // row-major); the first kLP are used
+  // Per-lane byte offsets of the load instructions (B, and A if row-major).
+  // With the 2-stage ring only those of instructions 0 and 1 are kept, and
+  // instruction j adds the uniform (j & ~1) * kRowsPerLoad * ld * 2 bytes
+  // (soff_j): fewer registers for a caller that keeps them live across an
+  // epilogue.  The deep ring keeps one offset per instruction.
+  static constexpr int kVa = kDeep ? kLP : 2;
+  uint32_t va[kVa];
+  uint32_t ldb;              // bytes per operand row (ld * 2)
   uint32_t aoff, boff;       // per-lane LDS byte offsets of fragment reads (step 0)
   char* smem;
   int wave;
@@ -225,11 +231,15 @@ struct GemmCoreT {
     // Load instruction q = wave*kLP + j moves rows [q*R, q*R + R)
     // (R = kRowsPerLoad); lane -> row q*R + lane/kChunks and LDS slot
     // lane%kChunks, which holds global chunk slot ^ swz(row).
+    // swz(row) depends on the row's low three bits (lane / kChunks for every
+    // j) and on bit 3, the parity of wave * kLP + j: instructions j and j & 1
+    // differ by a whole number of rows.
+    ldb = uint32_t(ld) * 2u;
 #pragma unroll
-    for (int j = 0; j < kLP; ++j) {
+    for (int j = 0; j < kVa; ++j) {
       const uint32_t row = uint32_t((wave * kLP + j) * kRowsPerLoad + lane / kChunks);
       const uint32_t chunk = uint32_t(lane % kChunks) ^ swz(row);
-      va[j] = row * uint32_t(ld) * 2u + chunk * 16u;
+      va[j] = row * ldb + chunk * 16u;
     }
     // Fragment rows are 32-aligned blocks + lane%32; swz depends on row mod 16.
     const uint32_t r32 = uint32_t(lane & 31);
@@ -246,9 +256,16 @@ struct GemmCoreT {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
+  // The per-lane offset of load instruction j, and its uniform part.
+  __device__ __forceinline__ uint32_t va_j(int j) const { return kDeep ? va[j] : va[j & 1]; }
+  __device__ __forceinline__ uint32_t soff_j(int j) const {
+    static_assert(kRowsPerLoad % 8 == 0, "the row swizzle depends on j through its parity only");
+    return kDeep ? 0u : uint32_t(j & ~1) * uint32_t(kRowsPerLoad) * ldb;
+  }
+
   // Load pair j (one A and one B instruction) of stage kt.
   __device__ __forceinline__ void load_pair(int kt, int j) {
-    const int soff = kt * kRowBytes;
+    const int soff = kt * kRowBytes + int(soff_j(j));
     char* s = smem + (kt % kStages) * kStageBytes;
     const int q = wave * kLP + j;
     if (ANative)  // piece q of the stage's contiguous 32 KB block, lane-major as stored
@@ -256,10 +273,10 @@ struct GemmCoreT {
                                                uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
                                                kt * kOpStageBytes, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j], soff, 0,
-                                               0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va_j(j), soff,
+                                               0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kOpStageBytes + q * 1024), 16,
-                                             va[j], soff, 0, 0);
+                                             va_j(j), soff, 0, 0);
   }
 
   // kDeep: A's and B's instructions of stage kt, each into its own ring.
@@ -271,14 +288,14 @@ struct GemmCoreT {
                                                uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
                                                kt * kOpStageBytes, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va[j],
-                                               kt * kRowBytes, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va_j(j),
+                                               kt * kRowBytes + int(soff_j(j)), 0, 0);
   }
   __device__ __forceinline__ void load_b(int kt, int j) {
     const int q = wave * kLP + j;
     char* s = smem + (3 + kt % 2) * kOpStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + q * 1024), 16, va[j],
-                                             kt * kRowBytes, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + q * 1024), 16, va_j(j),
+                                             kt * kRowBytes + int(soff_j(j)), 0, 0);
   }
 
   // Fragment read number q (0 .. kNR-1) into set F: A blocks first.
@@ -438,6 +455,44 @@ struct GemmCoreT {
     }
   }
 
+  // Persistent use (ring of kStages = 2, Pipe 0 or 1, operands row-major):
+  // a workgroup that computes tile after tile issues the next tile's first
+  // stage (issue_first, after retile) as soon as a tile's main loop is done,
+  // overlapping those loads with the tile's epilogue, then begin_tile()
+  // waits for them (and for every other memory operation of the wave),
+  // zeroes the accumulators and reads the first fragments, and mainloop()
+  // runs the stages.
+  __device__ __forceinline__ void retile(const uint16_t* A, int64_t a0, int64_t a_rows,
+                                         const uint16_t* B, int64_t b0, int64_t b_rows,
+                                         int64_t ld) {
+    static_assert(!ANative && !kDeep && kStages == 2, "persistent use: row-major 2-stage ring");
+    ra = tile_rsrc(A, a0, a_rows, ld);
+    rb = tile_rsrc(B, b0, b_rows, ld);
+  }
+  __device__ __forceinline__ void issue_first() {
+#pragma unroll
+    for (int j = 0; j < kLP; ++j) load_pair(0, j);
+  }
+  __device__ __forceinline__ void begin_tile() {
+    wait_loads_except(0);
+    barrier();
+#pragma unroll
+    for (int i = 0; i < kNA; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+#pragma unroll
+    for (int q = 0; q < kNR; ++q) read_one<0>(smem, aoff, boff, q);
+  }
+  __device__ __forceinline__ void mainloop(int K) {
+    nk = K / kBK;
+    int kt = 0;
+    for (; kt + 1 < nk; ++kt) stage<true, true>(kt);
+    stage<false, false>(kt);
+    barrier();
+  }
+
   // K must be a multiple of kBK.  Ends with no load in flight and, after the
   // trailing barrier, no LDS read outstanding, so the caller may reuse the LDS.
   __device__ __forceinline__ void run(int K) {
@@ -508,11 +563,21 @@ using GemmCore = GemmCoreT<false>;
 // dimension's operand streams past, and the workgroups resident on one XCD
 // share both.  The grid is padded to a multiple of 8; returns false for the
 // padding.
+__device__ __forceinline__ bool tile_at(uint64_t w, int64_t n_a, int64_t n_b, int64_t& ta,
+                                        int64_t& tb, int group = kRasterGroup);
+
 __device__ __forceinline__ bool tile_of(int64_t n_a, int64_t n_b, int64_t& ta, int64_t& tb,
                                         int group = kRasterGroup) {
   const uint64_t nb = gridDim.x;
   const uint64_t b = blockIdx.x;
   const uint64_t w = (b & 7) * (nb >> 3) + (b >> 3);
+  return tile_at(w, n_a, n_b, ta, tb, group);
+}
+
+// The tile at logical position w of the raster order described above (false
+// for the padding past the last tile).
+__device__ __forceinline__ bool tile_at(uint64_t w, int64_t n_a, int64_t n_b, int64_t& ta,
+                                        int64_t& tb, int group) {
   const uint64_t no = uint64_t(n_b);
   const uint64_t n_tiles = uint64_t(n_a) * no;
   if (w >= n_tiles) return false;

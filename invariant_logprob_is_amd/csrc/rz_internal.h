@@ -20,6 +20,7 @@ constexpr int kMaxH = 16384;
 constexpr int64_t kMaxV = 4000000;  // keeps a 256-row tile of the padded V below 2^31 bytes
 constexpr int64_t kBwdChunk = 32768;  // tokens per backward / learner-step chunk (bounds the P workspace)
 constexpr int kRasterGroup = 8;     // first-dimension tiles per L2 group in the tile raster
+constexpr int kFwdTickets = 8;      // per-XCD tile counters of the persistent forward
 
 // Raster group of the forward (vocabulary tiles visited for every token
 // tile).  The forward keeps two things in the MALL (256 MB): the W rows of
@@ -106,14 +107,14 @@ inline DwExactBufs dw_exact_bufs(void* base, int64_t tc, int64_t H) {
 // different entry points overlap (calls on one workspace are ordered).
 struct WsLayout {
   // rz_logprob (chunks of at most kBwdChunk tokens)
-  size_t hhat, pm, ps, ztgt, fwd_end;
+  size_t tick, hhat, pm, ps, ztgt, fwd_end;
   // rz_backward (chunks of at most kBwdChunk tokens)
-  size_t b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, b_rec, bwd_end;
+  size_t b_tick, b_hhat, b_wt, b_e, b_pm, b_ps, b_zt, b_d, b_g, b_rec, bwd_end;
   // rz_is_loss / rz_d3
   size_t part, flag, loss_end;
   // rz_learner_step (chunks of at most kBwdChunk tokens)
-  size_t s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_rec, s_cs, s_lse, s_coef, s_part,
-      s_flag, step_end;
+  size_t s_tick, s_hhat, s_wt, s_e, s_pm, s_ps, s_zt, s_d, s_g, s_rec, s_cs, s_lse, s_coef,
+      s_part, s_flag, step_end;
   // rz_learner_step with weight gradients: the step region, then these
   size_t g_hs, g_dw, g_rbuf, g_part, grads_end;
   size_t total;
@@ -126,12 +127,14 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
   const int64_t tcp = shift_stride(tc);
   size_t o = 0;
+  L.tick = o;  o = align256(o + kFwdTickets * 4);
   L.hhat = o;  o = align256(o + size_t(tc) * H * 2);
   L.pm = o;    o = align256(o + size_t(nvt) * tc * 4);
   L.ps = o;    o = align256(o + size_t(nvt) * tc * 4);
   L.ztgt = o;  o = align256(o + size_t(tc) * 4);
   L.fwd_end = o;
   o = 0;
+  L.b_tick = o; o = align256(o + kFwdTickets * 4);
   L.b_hhat = o; o = align256(o + size_t(tc) * H * 2);
   L.b_wt = o;   o = align256(o + size_t(H) * Vp * 2);
   L.b_e = o;    o = align256(o + size_t(tcp) * Vp * 2);
@@ -147,6 +150,7 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   L.flag = o;   o = align256(o + 4);
   L.loss_end = o;
   o = 0;
+  L.s_tick = o; o = align256(o + kFwdTickets * 4);
   L.s_hhat = o; o = align256(o + size_t(tc) * H * 2);
   L.s_wt = o;   o = align256(o + size_t(H) * Vp * 2);
   L.s_e = o;    o = align256(o + size_t(tcp) * Vp * 2);
@@ -203,15 +207,17 @@ struct ProfScope {
 // rstd (fp32 rounding of the float64 r of each row) may be null.
 hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float eps,
                               int64_t T, int H, uint16_t* hhat, float* rstd, hipStream_t s);
+// ticket: kFwdTickets ints of device memory for the persistent forward's
+// tile counters (reset by the launch).
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
-                             uint16_t* E, hipStream_t s);
+                             uint16_t* E, int* ticket, hipStream_t s);
 // The forward over the vocabulary rows [v0, v0 + Vs) of a model with V rows
 // in all (W points at row v0; targets are global row indices).  ztgt starts
 // at 0: only rows whose target lies in the range get their logit.
 hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                                    int64_t T, int H, int64_t v0, int Vs, float* pm, float* ps,
-                                   float* ztgt, hipStream_t s);
+                                   float* ztgt, int* ticket, hipStream_t s);
 // Per-split records (struct rz_vocab_split of rz.h) for splits [s0, s1) of a
 // model with V rows, from the tile partials of the range forward above
 // (whose first tile is split s0's); out[(s - s0) * out_stride + t].

@@ -222,6 +222,10 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 // computes M and S with the same code.
 // ---------------------------------------------------------------------------
 constexpr int kFwdPipe = 0;
+// The persistent forward (k_lmhead_fwd_p) instead of one workgroup per tile.
+constexpr bool kFwdPersistent = true;
+// Workgroups of the persistent forward: one per CU of the MI355X.
+constexpr int kFwdPersistentGrid = 256;
 // The GEMM ring + the exchange area; a ring that fills the LDS holds the
 // exchange area in its last 2 KB, used only after the ring's final barrier.
 constexpr int kFwdLds = kFwdPipe == 2 ? 5 * kOpStageBytes : kLdsBytes + 2048;
@@ -238,17 +242,24 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
                                              uint16_t* __restrict__ E) {
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // The lane-derived values are recomputed here from an opaque copy of the
+  // thread index rather than kept live from before the main loop, where a
+  // persistent caller cannot afford the registers.
+  int tid = int(threadIdx.x);
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int half = lane >> 5;
   const int col = lane & 31;
   float* xch = reinterpret_cast<float*>(lds + kFwdLds - 2048);
-  // rows of this lane below V: acc_row(wm, i, r, lane) < vlim
-  const int64_t vlim = int64_t(V) - v0;
+  // rows of this lane below V: acc_row(wm, i, r, lane) < V - v0, i.e. the
+  // block offset i*32 + 8*(r/4) + r%4 (a constant of the unrolled loops)
+  // below lim (the last tile only, so lim < 256)
+  const int lim = Mask ? int(int64_t(V) - v0) - (wm * 128 + 4 * (lane >> 5)) : 0;
   auto val = [&](int i, int j, int r) -> float {
-    return (!Mask || acc_row(wm, i, r, lane) < vlim) ? acc[i][j][r] : -INFINITY;
+    return (!Mask || i * 32 + 8 * (r >> 2) + (r & 3) < lim) ? acc[i][j][r] : -INFINITY;
   };
 
   // 1. tile max
@@ -344,33 +355,38 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
 // the accumulators live in VGPRs, which the epilogue reads directly.
 constexpr int kFwdWaves = 8;
 
-template <bool Store>
-__global__ __launch_bounds__(64 * kFwdWaves)
-__attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
-void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
-                  const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
-                  int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
-                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E, int raster_group) {
-  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
-  int64_t tt, vt;
-  // Vocabulary tiles are grouped (raster_group of them, chosen on the host
-  // from H so that the group's W rows and the chunk's hhat fit the MALL
-  // together) and the token tiles stream past them: the chunk's hhat
-  // (100 MB at H = 1536) stays cache-resident across the groups, where
-  // re-streaming W (467 MB) from HBM for every token group would not.
-  if (!tile_of(n_vt, n_tt, vt, tt, raster_group)) return;
+// The targets of the lane's token columns of token tile tt (0 past T), as
+// stored.  Loaded before the main loop and used only in the epilogue, so the
+// epilogue issues no load that the memory operations in flight would have to
+// drain for.
+template <int NB>
+__device__ __forceinline__ void fwd_targets(const int32_t* __restrict__ target, int64_t tt,
+                                            int64_t T, int32_t (&tg)[NB]) {
+  const int lane = threadIdx.x & 63;
+  const int wn = (threadIdx.x >> 6) >> 1;
+#pragma unroll
+  for (int j = 0; j < NB; ++j) {
+    const int64_t t = tt * kTile + acc_col(wn, j, lane, NB);
+    tg[j] = t < T ? target[t] : 0;
+  }
+}
+
+// The epilogue of one forward tile (vocabulary tile vt, token tile tt) on its
+// accumulators: the target gather (tg from fwd_targets), then the tile's
+// partials and (Store) the stored e.
+template <bool Store, int NB>
+__device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NB], char* lds, int64_t tt,
+                                             int64_t vt, const int32_t (&tgs)[NB],
+                                             int64_t tgt_off, int64_t T, int V, int64_t Vp,
+                                             float* __restrict__ pm,
+                                             float* __restrict__ ps, float* __restrict__ ztgt,
+                                             uint16_t* __restrict__ E) {
   const int64_t v0 = vt * kTile;
   const int64_t t0 = tt * kTile;
-  using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
-  static_assert(Core::kLds <= kFwdLds, "LDS");
-  constexpr int NB = Core::kNB;
-  Core g;
-  g.init(W, v0, V, hhat, t0, T, H, lds);
-  g.run(H);
-  f32x16 (&acc)[4][NB] = g.acc;
-
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  int tid = int(threadIdx.x);
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
   const int wm = wave & 1;
   const int wn = wave >> 1;
   const int half = lane >> 5;
@@ -382,7 +398,7 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   for (int j = 0; j < NB; ++j) {
     const int64_t t = t0 + acc_col(wn, j, lane, NB);
     if (t < T) {
-      const int64_t tg = int64_t(target[t]) - tgt_off;
+      const int64_t tg = int64_t(tgs[j]) - tgt_off;
       const int64_t loc = tg - vbase;
       if (tg >= 0 && tg < V && loc >= 0 && loc < 128) {
         const int q = int(loc & 31);
@@ -405,6 +421,93 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
     fwd_tile_lse<Store, true>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
   else
     fwd_tile_lse<Store, false>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
+}
+
+template <bool Store>
+__global__ __launch_bounds__(64 * kFwdWaves)
+__attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
+void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
+                  const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
+                  int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
+                  float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E, int raster_group) {
+  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
+  int64_t tt, vt;
+  // Vocabulary tiles are grouped (raster_group of them, chosen on the host
+  // from H so that the group's W rows and the chunk's hhat fit the MALL
+  // together) and the token tiles stream past them: the chunk's hhat
+  // (100 MB at H = 1536) stays cache-resident across the groups, where
+  // re-streaming W (467 MB) from HBM for every token group would not.
+  if (!tile_of(n_vt, n_tt, vt, tt, raster_group)) return;
+  using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
+  static_assert(Core::kLds <= kFwdLds, "LDS");
+  Core g;
+  int32_t tg[Core::kNB];
+  fwd_targets<Core::kNB>(target, tt, T, tg);
+  g.init(W, vt * kTile, V, hhat, tt * kTile, T, H, lds);
+  g.run(H);
+#pragma unroll
+  for (int j = 0; j < Core::kNB; ++j) asm volatile("" : "+v"(tg[j]));
+  fwd_epilogue<Store, Core::kNB>(g.acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt, E);
+}
+
+// The same forward with one workgroup per CU: each takes the logical tile
+// positions of its XCD's range of the raster order (workgroup b runs on XCD
+// b % 8) from that XCD's counter, ticket[b % 8], so the XCD's workgroups run
+// the range in the order a relaunched grid would, and it issues the next
+// tile's first stage as soon as a tile's main loop is done, so those loads
+// overlap the tile's epilogue instead of following a relaunch.  The counter
+// of the next tile is fetched while the main loop runs.  Which workgroup
+// computes a tile changes no bit of it.
+template <bool Store>
+__global__ __launch_bounds__(64 * kFwdWaves)
+__attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
+void k_lmhead_fwd_p(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
+                    const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
+                    int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
+                    float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E,
+                    int raster_group, int64_t n_logical, int* __restrict__ ticket) {
+  // One LDS object: the ticket broadcast lives past the ring and the
+  // exchange area.  A second __shared__ variable would give LDS accesses
+  // alias scopes, and the compiler then waits for every LDS-direct load in
+  // flight before each fragment read of the main loop.
+  __shared__ __attribute__((aligned(16))) char lds[kFwdLds + 16];
+  int& nextk = *reinterpret_cast<int*>(lds + kFwdLds);
+  using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
+  const int x = blockIdx.x & 7;
+  const int64_t per = n_logical >> 3;
+  if (threadIdx.x == 0) nextk = atomicAdd(ticket + x, 1);
+  __syncthreads();
+  int64_t vt, tt;
+  if (nextk >= per || !tile_at(uint64_t(x * per + nextk), n_vt, n_tt, vt, tt, raster_group)) return;
+  Core g;
+  int32_t tg[Core::kNB];
+  g.init(W, vt * kTile, V, hhat, tt * kTile, T, H, lds);
+  g.issue_first();
+  while (true) {
+    g.begin_tile();
+    fwd_targets<Core::kNB>(target, tt, T, tg);
+    int k = 0;
+    if (threadIdx.x == 0) k = atomicAdd(ticket + x, 1);
+    g.mainloop(H);
+    // the targets and the counter are first used here: their loads have
+    // completed during the main loop, and nothing before it waits for them
+#pragma unroll
+    for (int j = 0; j < Core::kNB; ++j) asm volatile("" : "+v"(tg[j]));
+    if (threadIdx.x == 0) nextk = k;
+    Core::barrier();
+    k = nextk;
+    int64_t nvt = 0, ntt = 0;
+    const bool more = k < per && tile_at(uint64_t(x * per + k), n_vt, n_tt, nvt, ntt,
+                                         raster_group);
+    if (more) {
+      g.retile(W, nvt * kTile, V, hhat, ntt * kTile, T, H);
+      g.issue_first();
+    }
+    fwd_epilogue<Store, Core::kNB>(g.acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt, E);
+    if (!more) break;
+    vt = nvt;
+    tt = ntt;
+  }
 }
 
 // Shift table and row factor that turn the stored e of a token back into its
@@ -619,6 +722,11 @@ __global__ __launch_bounds__(256) void k_shift_prep(const float* __restrict__ pm
   const int64_t t = int64_t(blockIdx.x) * 256 + threadIdx.x;
   if (t >= T) return;
   shift_tables(pm, T, n_vt, t, tile_ref(max_tile_max(pm, T, n_vt, t)), lse[t], D, ds, g);
+}
+
+__global__ void k_fill_i32(int32_t* p, int64_t n, int32_t v) {
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
 }
 
 __global__ void k_fill_f32(float* p, int64_t n, float v) {
@@ -1155,35 +1263,51 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float ep
   return hipGetLastError();
 }
 
+// Launches the forward over n_vt x n_tt tiles, relaunched per tile or
+// persistent (ticket: kFwdTickets ints of device memory).
+template <bool Store>
+static void launch_fwd_grid(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
+                            int64_t tgt_off, int64_t T, int H, int V, int64_t n_vt, int64_t n_tt,
+                            float* pm, float* ps, float* ztgt, uint16_t* E, int* ticket,
+                            hipStream_t s) {
+  const uint32_t nl = raster_grid(n_vt * n_tt);
+  if (kFwdPersistent) {
+    hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, s, ticket, int64_t(kFwdTickets), 0);
+    const uint32_t grid = nl < uint32_t(kFwdPersistentGrid) ? nl : uint32_t(kFwdPersistentGrid);
+    hipLaunchKernelGGL(k_lmhead_fwd_p<Store>, dim3(grid), dim3(64 * kFwdWaves), 0, s, hhat, W,
+                       target, tgt_off, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E,
+                       fwd_raster_group(H), int64_t(nl), ticket);
+  } else {
+    hipLaunchKernelGGL(k_lmhead_fwd<Store>, dim3(nl), dim3(64 * kFwdWaves), 0, s, hhat, W, target,
+                       tgt_off, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E,
+                       fwd_raster_group(H));
+  }
+}
+
 hipError_t launch_lmhead_fwd(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                              int64_t T, int H, int V, float* pm, float* ps, float* ztgt,
-                             uint16_t* E, hipStream_t s) {
+                             uint16_t* E, int* ticket, hipStream_t s) {
   ProfScope prof("k_lmhead_fwd", s);
   const int64_t n_vt = n_vocab_tiles(V);
   const int64_t n_tt = ceil_div(T, kTile);
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, NAN);
   if (E)
-    hipLaunchKernelGGL(k_lmhead_fwd<true>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
-                       hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
-                       ztgt, E, fwd_raster_group(H));
+    launch_fwd_grid<true>(hhat, W, target, 0, T, H, V, n_vt, n_tt, pm, ps, ztgt, E, ticket, s);
   else
-    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
-                       hhat, W, target, int64_t(0), T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps,
-                       ztgt, E, fwd_raster_group(H));
+    launch_fwd_grid<false>(hhat, W, target, 0, T, H, V, n_vt, n_tt, pm, ps, ztgt, E, ticket, s);
   return hipGetLastError();
 }
 
 hipError_t launch_lmhead_fwd_range(const uint16_t* hhat, const uint16_t* W, const int32_t* target,
                                    int64_t T, int H, int64_t v0, int Vs, float* pm, float* ps,
-                                   float* ztgt, hipStream_t s) {
+                                   float* ztgt, int* ticket, hipStream_t s) {
   ProfScope prof("k_lmhead_fwd", s);
   const int64_t n_vt = n_vocab_tiles(Vs);
   const int64_t n_tt = ceil_div(T, kTile);
   hipLaunchKernelGGL(k_fill_f32, dim3(blocks_for(T, 256)), dim3(256), 0, s, ztgt, T, 0.0f);
   if (n_vt > 0)
-    hipLaunchKernelGGL(k_lmhead_fwd<false>, dim3(raster_grid(n_vt * n_tt)), dim3(64 * kFwdWaves), 0, s,
-                       hhat, W, target, v0, T, H, Vs, n_vt, n_tt, vocab_pad(Vs), pm, ps, ztgt,
-                       static_cast<uint16_t*>(nullptr), fwd_raster_group(H));
+    launch_fwd_grid<false>(hhat, W, target, v0, T, H, Vs, n_vt, n_tt, pm, ps, ztgt, nullptr,
+                           ticket, s);
   return hipGetLastError();
 }
 
