@@ -256,16 +256,19 @@ struct GemmCoreT {
         for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
-  // The per-lane offset of load instruction j, and its uniform part.
+  // The per-lane offset of load instruction j, and its uniform part.  The
+  // callers copy them into locals before the load builtin: with a member
+  // call among its operands the builtin fails overload resolution in
+  // hipcc's host pass.
   __device__ __forceinline__ uint32_t va_j(int j) const { return kDeep ? va[j] : va[j & 1]; }
   __device__ __forceinline__ uint32_t soff_j(int j) const {
-    static_assert(kRowsPerLoad % 8 == 0, "the row swizzle depends on j through its parity only");
     return kDeep ? 0u : uint32_t(j & ~1) * uint32_t(kRowsPerLoad) * ldb;
   }
 
   // Load pair j (one A and one B instruction) of stage kt.
   __device__ __forceinline__ void load_pair(int kt, int j) {
     const int soff = kt * kRowBytes + int(soff_j(j));
+    const uint32_t vo = va_j(j);
     char* s = smem + (kt % kStages) * kStageBytes;
     const int q = wave * kLP + j;
     if (ANative)  // piece q of the stage's contiguous 32 KB block, lane-major as stored
@@ -273,29 +276,30 @@ struct GemmCoreT {
                                                uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
                                                kt * kOpStageBytes, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va_j(j), soff,
-                                               0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, vo, soff, 0, 0);
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kOpStageBytes + q * 1024), 16,
-                                             va_j(j), soff, 0, 0);
+                                             vo, soff, 0, 0);
   }
 
   // kDeep: A's and B's instructions of stage kt, each into its own ring.
   __device__ __forceinline__ void load_a(int kt, int j) {
     const int q = wave * kLP + j;
     char* s = smem + (kt % 3) * kOpStageBytes;
+    const uint32_t vo = va_j(j);
+    const int soff = kt * kRowBytes + int(soff_j(j));
     if (ANative)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
                                                uint32_t(q * 1024 + (threadIdx.x & 63) * 16),
                                                kt * kOpStageBytes, 0, 0);
     else
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, va_j(j),
-                                               kt * kRowBytes + int(soff_j(j)), 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, vo, soff, 0, 0);
   }
   __device__ __forceinline__ void load_b(int kt, int j) {
     const int q = wave * kLP + j;
     char* s = smem + (3 + kt % 2) * kOpStageBytes;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + q * 1024), 16, va_j(j),
-                                             kt * kRowBytes + int(soff_j(j)), 0, 0);
+    const uint32_t vo = va_j(j);
+    const int soff = kt * kRowBytes + int(soff_j(j));
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + q * 1024), 16, vo, soff, 0, 0);
   }
 
   // Fragment read number q (0 .. kNR-1) into set F: A blocks first.
