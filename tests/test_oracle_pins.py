@@ -453,11 +453,27 @@ def test_backward_invariants():
     np.testing.assert_allclose(np.sum(xv * dxe, axis=1), 0.0, atol=1e-12)
 
 
-def test_learner_step_tiny_is_finite_and_consistent():
+def test_learner_step_wires_the_pinned_stages():
+    """learner_step is the composition of stages pinned one by one above
+    (rmsnorm, logprob, is_loss, d3, backward): every output must equal the
+    stage it comes from, bit for bit, and the on-policy case must reduce to
+    its closed forms (D3 = 0, w = 1)."""
     b = workloads.tiny()
     lp, lse = oracle.logprob(b.x, b.gamma, b.eps, b.W, b.target)
     mu = lp + b.lag_noise.astype(np.float64)
-    out = oracle.learner_step(b.x, b.gamma, b.eps, b.W, b.target, mu, b.resp_offsets, b.group_offsets, b.reward)
-    assert np.all(np.isfinite(out["dhidden"]))
+    out = oracle.learner_step(b.x, b.gamma, b.eps, b.W, b.target, mu, b.resp_offsets,
+                              b.group_offsets, b.reward)
     np.testing.assert_array_equal(out["logprob"], lp)
+    np.testing.assert_array_equal(out["lse"], lse)
+    L = oracle.is_loss(lp, mu, b.resp_offsets, b.group_offsets, b.reward)
+    for k in ("coef", "advantage", "w"):
+        np.testing.assert_array_equal(out[k], L[k])
+    assert out["loss"] == L["loss"]
+    assert out["d3"] == oracle.d3(lp, mu)
+    np.testing.assert_array_equal(
+        out["dhidden"], oracle.backward(b.x, b.gamma, b.eps, b.W, b.target, lse, L["coef"]))
     assert out["d3"] == pytest.approx(0.01 ** 2 / 2, rel=0.3)
+    on = oracle.learner_step(b.x, b.gamma, b.eps, b.W, b.target, lp, b.resp_offsets,
+                             b.group_offsets, b.reward)
+    assert on["d3"] == 0.0
+    np.testing.assert_array_equal(on["w"], 1.0)
