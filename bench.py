@@ -29,7 +29,7 @@ PEAK_HBM_BYTES = 8.0e12
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = [
     os.path.join(ROOT, "invariant_logprob_is_amd", "csrc", f)
-    for f in ("rz_kernels.hip", "rz_gemm.h", "rz_gemm_tr.h", "rz_internal.h")
+    for f in ("rz_kernels.hip", "rz_gemm.h", "rz_gemm_tr.h", "rz_internal.h", "rz_util.h")
 ]
 
 
@@ -232,9 +232,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, dram_csv: str = None):
                 max(dwr.get(copy, [0.0])) / CALIBRATION_BYTES)
     os.makedirs(PROFILES, exist_ok=True)
     sha = source_sha()
-    # the learner step launches the storing forward variant; k_dw (--grads)
-    # is the row scaling plus the token contraction, one of each per chunk
-    for k, disps in (("k_lmhead_fwd", ("k_lmhead_fwd<true>",)), ("k_dhidden", ("k_dhidden",)),
+    # the learner step launches the storing forward variant (persistent, or
+    # one workgroup per tile); k_dw (--grads) is the row scaling plus the
+    # token contraction, one of each per chunk
+    fwd = "k_lmhead_fwd_p<true>" if "k_lmhead_fwd_p<true>" in fetch else "k_lmhead_fwd<true>"
+    for k, disps in (("k_lmhead_fwd", (fwd,)), ("k_dhidden", ("k_dhidden",)),
                      ("k_dw", ("k_scale_rows_t", "k_dw_tr"))):
         if any(d not in fetch or d not in write for d in disps):
             continue

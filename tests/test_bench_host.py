@@ -63,3 +63,54 @@ def test_bench_refuses_more_than_one_gpu():
     p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True)
     assert p.returncode == 2 and "one GPU" in p.stdout
+
+
+def _counter_csv(path, rows):
+    import csv
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=["Dispatch_Id", "Kernel_Name", "Counter_Name",
+                                          "Counter_Value"])
+        w.writeheader()
+        for r in rows:
+            w.writerow(dict(zip(w.fieldnames, r)))
+
+
+def test_summarize_counters_scales_by_the_copy_and_maps_kernels(tmp_path, monkeypatch):
+    """FETCH_SIZE / WRITE_SIZE arrive in KiB per dispatch and are divided by
+    what the calibration copy reads; the DRAM request counters are divided by
+    the copy's requests per byte.  The persistent forward's dispatches are
+    the forward's, and k_dw adds the row scaling to the token contraction."""
+    C = bench.CALIBRATION_BYTES
+    kib = 1024.0
+    copy = "__amd_rocclr_copyBuffer"
+    fwd = "void rz::k_lmhead_fwd_p<true>(unsigned short const*, ...)"
+    fetch = [(1, copy, "FETCH_SIZE", 0.5 * C / kib),
+             (2, fwd, "FETCH_SIZE", 0.5 * 3e9 / kib), (3, fwd, "FETCH_SIZE", 0.5 * 5e9 / kib),
+             (4, "rz::k_dhidden(...)", "FETCH_SIZE", 0.5 * 2e9 / kib),
+             (5, "rz::k_scale_rows_t(...)", "FETCH_SIZE", 0.5 * 1e9 / kib),
+             (6, "rz::k_dw_tr(...)", "FETCH_SIZE", 0.5 * 7e9 / kib)]
+    write = [(1, copy, "WRITE_SIZE", C / kib), (2, fwd, "WRITE_SIZE", 1e9 / kib),
+             (3, fwd, "WRITE_SIZE", 1e9 / kib), (4, "rz::k_dhidden(...)", "WRITE_SIZE", 2e9 / kib),
+             (5, "rz::k_scale_rows_t(...)", "WRITE_SIZE", 0.0),
+             (6, "rz::k_dw_tr(...)", "WRITE_SIZE", 4e9 / kib)]
+    dram = [(1, copy, "TCC_EA0_RDREQ_DRAM_sum", C / 128), (1, copy, "TCC_EA0_WRREQ_DRAM_sum", C / 64),
+            (2, fwd, "TCC_EA0_RDREQ_DRAM_sum", 6e9 / 128), (2, fwd, "TCC_EA0_WRREQ_DRAM_sum", 2e9 / 64),
+            (3, fwd, "TCC_EA0_RDREQ_DRAM_sum", 2e9 / 128), (3, fwd, "TCC_EA0_WRREQ_DRAM_sum", 0.0)]
+    paths = [str(tmp_path / n) for n in ("f.csv", "w.csv", "d.csv")]
+    for p, rows in zip(paths, (fetch, write, dram)):
+        _counter_csv(p, rows)
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path / "profiles"))
+    bench.summarize_counters(*paths)
+    import json
+    f = json.load(open(tmp_path / "profiles" / "traffic_k_lmhead_fwd.json"))
+    assert f["launches"] == 2
+    assert abs(f["fetch_bytes_per_launch"] - 4e9) < 1e3
+    assert abs(f["write_bytes_per_launch"] - 1e9) < 1e3
+    assert abs(f["dram_read_bytes_per_launch"] - 4e9) < 1e3
+    assert abs(f["dram_write_bytes_per_launch"] - 1e9) < 1e3
+    assert f["source_sha"] == bench.source_sha()
+    d = json.load(open(tmp_path / "profiles" / "traffic_k_dhidden.json"))
+    assert abs(d["bytes_per_launch"] - 4e9) < 1e3 and "dram_read_bytes_per_launch" not in d
+    w = json.load(open(tmp_path / "profiles" / "traffic_k_dw.json"))
+    assert abs(w["fetch_bytes_per_launch"] - 8e9) < 1e3
+    assert abs(w["write_bytes_per_launch"] - 4e9) < 1e3
