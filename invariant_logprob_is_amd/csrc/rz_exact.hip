@@ -185,8 +185,10 @@ __global__ __launch_bounds__(kSelThreads) void k_select(
       for (int e = 0; e < 8; ++e) {
         const uint16_t bits = uint16_t(raw[e >> 1] >> (16 * (e & 1)));
         const float pp = bf16_to_f32(shift_bits(bits, dd));
-        val[k * 8 + e] =
-            (vb[k] >= 0 && pp > 0.0f && double(gt) * double(pp) >= tpv) ? pp : -1.0f;
+        // rows past V hold e = 0 as the forward stores them; the row bound
+        // keeps a selection in W's rows whatever the stored values
+        val[k * 8 + e] = (vb[k] >= 0 && vb[k] + e < V && pp > 0.0f &&
+                          double(gt) * double(pp) >= tpv) ? pp : -1.0f;
       }
     }
     // kSelK rounds: the largest remaining operand of the wave (ties: lower

@@ -288,6 +288,22 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
   // block at a time to keep few values live.
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   const int64_t n_ks = Vp / 16;
+  // The e of this (token tile, vocabulary tile) pair is one contiguous block
+  // of 16 steps x 8 fragments: the stores address it from a uniform base
+  // with 32-bit offsets (a per-lane part and a constant per store).  Steps at
+  // or past n_ks exist only in the last vocabulary tile; a wave's steps are
+  // wm*8 .. wm*8+7, so the check is uniform per wave.
+  char* eb = nullptr;
+  uint32_t evo = 0;
+  int nvs = 0;   // valid steps of this wave's eight
+  if (Store) {
+    const int64_t ks_first = v0 / 16;
+    eb = reinterpret_cast<char*>(E) + frag_offset(tt, ks_first, 0, n_ks);
+    evo = uint32_t(lane * 16 + wn * NB * 1024 + wm * 8 * 8 * 1024);
+    const int64_t tile_steps = n_ks - ks_first;    // >= 1
+    const int left = int(tile_steps < 16 ? tile_steps : 16) - __builtin_amdgcn_readfirstlane(wm) * 8;
+    nvs = __builtin_amdgcn_readfirstlane(left < 0 ? 0 : left);
+  }
   float Sj[NB];
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
@@ -312,7 +328,6 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
         }
       }
       if (Store) {
-        const int64_t ks0 = (v0 + wm * 128 + i * 32) / 16;
 #pragma unroll
         for (int qp = 0; qp < 2; ++qp) {
           const auto d0 = __builtin_amdgcn_permlane32_swap(X[2 * qp][0], X[2 * qp + 1][0], false, false);
@@ -322,11 +337,10 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
           f[1] = d1[0];
           f[2] = d0[1];
           f[3] = d1[1];
-          const int64_t ks = ks0 + qp;
-          if (ks < n_ks)
-            __builtin_nontemporal_store(
-                f, reinterpret_cast<u32x4*>(reinterpret_cast<char*>(E) +
-                                            frag_offset(tt, ks, wn * NB + j, n_ks) + lane * 16));
+          // step wm*8 + 2i + qp of the block, fragment wn*NB + j
+          const uint32_t soff = uint32_t(((i * 2 + qp) * 8 + j) * 1024);
+          if (i * 2 + qp < nvs)
+            __builtin_nontemporal_store(f, reinterpret_cast<u32x4*>(eb + (evo + soff)));
         }
       }
     }
