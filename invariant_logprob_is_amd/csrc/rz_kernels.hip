@@ -3,6 +3,8 @@
 // row sees is exactly what is written.
 #include <math.h>
 
+#include <atomic>
+
 #include "rz_gemm.h"
 #include "rz_gemm_tr.h"
 #include "rz_util.h"
@@ -224,8 +226,11 @@ __global__ __launch_bounds__(256) void k_rmsnorm_bwd(const uint16_t* __restrict_
 constexpr int kFwdPipe = 0;
 // The persistent forward (k_lmhead_fwd_p) instead of one workgroup per tile.
 constexpr bool kFwdPersistent = true;
-// Workgroups of the persistent forward: one per CU of the MI355X.
-constexpr int kFwdPersistentGrid = 256;
+// Workgroups of the persistent forward: one per CU of the device (256 on
+// an MI355X in its whole-chip mode), rounded down to a multiple of the 8
+// per-XCD counters.
+constexpr int kFwdPersistentGridMax = 256;
+constexpr int kMaxDevices = 64;
 // The GEMM ring + the exchange area; a ring that fills the LDS holds the
 // exchange area in its last 2 KB, used only after the ring's final barrier.
 constexpr int kFwdLds = kFwdPipe == 2 ? 5 * kOpStageBytes : kLdsBytes + 2048;
@@ -1277,6 +1282,27 @@ hipError_t launch_rmsnorm_fwd(const uint16_t* x, const uint16_t* gamma, float ep
   return hipGetLastError();
 }
 
+// The persistent forward's grid: the current device's CU count, looked up
+// once per device, as a multiple of the kFwdTickets counters.  Every
+// counter then has workgroups of its own (the workgroups of counter x are
+// those with blockIdx % 8 == x), whatever the count.
+static int persistent_grid() {
+  static std::atomic<int> cache[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return kFwdPersistentGridMax;
+  int g = cache[dev].load(std::memory_order_relaxed);
+  if (g > 0) return g;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = kFwdPersistentGridMax;
+  g = cus - cus % kFwdTickets;
+  if (g < kFwdTickets) g = kFwdTickets;
+  if (g > kFwdPersistentGridMax) g = kFwdPersistentGridMax;
+  cache[dev].store(g, std::memory_order_relaxed);
+  return g;
+}
+
 // Launches the forward over n_vt x n_tt tiles, relaunched per tile or
 // persistent (ticket: kFwdTickets ints of device memory).
 template <bool Store>
@@ -1287,7 +1313,8 @@ static void launch_fwd_grid(const uint16_t* hhat, const uint16_t* W, const int32
   const uint32_t nl = raster_grid(n_vt * n_tt);
   if (kFwdPersistent) {
     hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, s, ticket, int64_t(kFwdTickets), 0);
-    const uint32_t grid = nl < uint32_t(kFwdPersistentGrid) ? nl : uint32_t(kFwdPersistentGrid);
+    const uint32_t cap = uint32_t(persistent_grid());
+    const uint32_t grid = nl < cap ? nl : cap;
     hipLaunchKernelGGL(k_lmhead_fwd_p<Store>, dim3(grid), dim3(64 * kFwdWaves), 0, s, hhat, W,
                        target, tgt_off, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt, E,
                        fwd_raster_group(H), int64_t(nl), ticket);
