@@ -45,7 +45,19 @@ __device__ __forceinline__ u32x2 ds_read_tr16(uint32_t lds_addr) {
   return r;
 }
 
-struct GemmCoreTr {
+// NW: 4 waves (one per SIMD), each owning 128 vocabulary rows x 128 hidden
+// columns (4 x 4 blocks), or 8 waves (two per SIMD), each owning 64 x 128
+// (2 x 4 blocks): waves wm = w % kWM along the vocabulary, wn = w / kWM
+// along the hidden dimension.
+template <int NW>
+struct GemmCoreTrT {
+  static_assert(NW == 4 || NW == 8, "4 or 8 waves");
+  static constexpr int kNA = NW == 4 ? 4 : 2;  // A (vocabulary) blocks per wave
+  static constexpr int kNB = 4;                // B (hidden) blocks per wave
+  static constexpr int kWM = 8 / kNA;          // waves along the vocabulary
+  static constexpr int kNM = kNA * kNB;        // MFMAs per k-step
+  static constexpr int kNR = kNA + kNB;        // read units per k-step
+  static constexpr int kLPw = 32 / NW;         // load pairs per wave per stage
   static constexpr int kA = 32768;            // A stage bytes (32 fragments)
   static constexpr int kB = 32768;            // B stage bytes
   static constexpr int kD = 256;              // shift bytes per stage
@@ -55,14 +67,14 @@ struct GemmCoreTr {
   __amdgpu_buffer_rsrc_t ra, rb, rd;
   const char* e_tile0;    // e fragments of (token tile 0, vocabulary step vt*16)
   int64_t e_tile_stride;  // bytes between token tiles in the e block
-  uint32_t va[2], vb[8];  // per-lane load offsets (A within a fragment, even/odd step; B rows)
+  uint32_t va[2], vb[kLPw];  // per-lane load offsets (A within a fragment, even/odd step; B rows)
   uint32_t boff;          // per-lane LDS offset of the B fragment reads (k-step 0)
   char* smem;
   int wave, nk, a_range;
-  uint32_t a_rd[4][2];              // per-lane LDS byte offsets of the tr reads (k-step 0)
+  uint32_t a_rd[kNA][2];            // per-lane LDS byte offsets of the tr reads (k-step 0)
   uint32_t d_rd;                    // LDS offset of the lane's 8 token shifts (k-step 0)
-  f32x16 acc[4][4];
-  u32x4 fa[2][4], fb[2][4];  // fragments (8 bf16 each) as read
+  f32x16 acc[kNA][kNB];
+  u32x4 fa[2][kNA], fb[2][kNB];  // fragments (8 bf16 each) as read
   uint32_t lds_base;         // LDS address of smem
   u16x8 sh[2];            // per-set exponent shifts (d << 7) of the lane's 8 tokens
   u32x4 shr[2][2];        // the same as read from LDS (one token per 32-bit word)
@@ -77,8 +89,8 @@ struct GemmCoreTr {
     lds_base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)lds));
     const int lane = threadIdx.x & 63;
     wave = __builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6));
-    const int wm = wave & 1;
-    const int wn = wave >> 1;
+    const int wm = wave % kWM;
+    const int wn = wave / kWM;
     e_tile0 = reinterpret_cast<const char*>(E) + frag_offset(0, vt * 16, 0, n_ks);
     e_tile_stride = n_ks * 8 * 1024;
     // the last vocabulary tile may hold fewer than 16 steps (the vocabulary is
@@ -103,11 +115,11 @@ struct GemmCoreTr {
       const int L = lane ^ (8 * o);
       va[o] = uint32_t(((L >> 3) << 2) + (L & 3) + 32 * ((L >> 2) & 1)) * 16u;
     }
-    // B load q = wave*8 + u: rows 8q .. 8q+7, lane -> row 8q + lane/8, LDS
+    // B load q = wave*kLPw + u: rows 8q .. 8q+7, lane -> row 8q + lane/8, LDS
     // slot lane%8 holding the row's chunk (lane%8) ^ swz(row)
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint32_t row = uint32_t((wave * 8 + u) * 8 + lane / 8);
+    for (int u = 0; u < kLPw; ++u) {
+      const uint32_t row = uint32_t((wave * kLPw + u) * 8 + lane / 8);
       vb[u] = row * uint32_t(TCp) * 2u + ((uint32_t(lane % 8) ^ swz(row)) * 16u);
     }
     {
@@ -117,19 +129,24 @@ struct GemmCoreTr {
     // tr-read addresses for k-step 0 (read_step adds the k-step's offsets)
     const int g = lane >> 4, s = lane & 15, q = s >> 2, j = s & 3;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < kNA; ++i)
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        // A block i of wave wm: vocabulary step wm*8 + 2i + g%2 of the tile,
-        // token t = 8*(g/2) + 4h + q of the k-step
-        const int ksl = wm * 8 + 2 * i + (g & 1);
+        // A block i of wave wm: vocabulary step wm*2*kNA + 2i + g%2 of the
+        // tile, token t = 8*(g/2) + 4h + q of the k-step
+        const int ksl = wm * 2 * kNA + 2 * i + (g & 1);
         const int t = 8 * (g >> 1) + 4 * h + q;
         const int slot = ((t >> 2) * 8 + (j >> 1) * 4 + (t & 3)) ^ (8 * (ksl & 1));
         a_rd[i][h] = uint32_t(ksl * 2 * 1024 + slot * 16 + 8 * (j & 1));
       }
     // the lane's 8 token shifts: tokens 8*(lane/32) .. +7 of the k-step
     d_rd = uint32_t(kA + kB + (lane >> 5) * 8 * 4);
-    zero_acc(acc);
+#pragma unroll
+    for (int i = 0; i < kNA; ++i)
+#pragma unroll
+      for (int j = 0; j < kNB; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   }
 
   __device__ __forceinline__ void set_a_tile(int64_t tt) {
@@ -140,17 +157,20 @@ struct GemmCoreTr {
                                            __builtin_amdgcn_readfirstlane(a_range), kBufferFlags);
   }
 
-  // Loads of stage kt: pair u (0..7) = A fragment and B piece q = wave*8 + u;
-  // wave 0 also loads the stage's shifts with pair 0.
+  // Loads of stage kt: pair u (0..kLPw-1) = A fragment and B piece
+  // q = wave*kLPw + u; wave 0 also loads the stage's shifts with pair 0.
   __device__ __forceinline__ void load_pair(int kt, int u) {
     char* s = smem + (kt & 1) * kStage;
-    const int q = wave * 8 + u;
+    const int q = wave * kLPw + u;
     // A fragment q: vocabulary step q/2, token block 2*(kt%4) + q%2 of the tile
     const int soffA = ((kt & 3) * 2) * 1024;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16,
-                                             uint32_t((q >> 1) * 8192 + (q & 1) * 1024) + va[(u >> 1) & 1],
-                                             soffA, 0, 0);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16, vb[u],
+    // (the operands go through locals: hipcc's host pass rejects member
+    // arrays of a dependent size among the builtin's operands)
+    const uint32_t voa = uint32_t((q >> 1) * 8192 + (q & 1) * 1024) + va[(u >> 1) & 1];
+    const uint32_t vob = vb[u];
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(s + q * 1024), 16, voa, soffA, 0,
+                                             0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(s + kA + q * 1024), 16, vob,
                                              kt * 128, 0, 0);
     if (u == 0 && wave == 0)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rd, (lds_void_t*)(s + kA + kB), 4,
@@ -162,18 +182,18 @@ struct GemmCoreTr {
     return uint32_t((kk >> 1) * 1024 + (kk & 1) * 4 * 8 * 16);
   }
 
-  // Read unit u (0..7) of k-step kk into set F: A block u (u < 4, two
-  // transposing reads) or B block u - 4 (one 16-byte read).
+  // Read unit u (0..kNR-1) of k-step kk into set F: A block u (u < kNA, two
+  // transposing reads) or B block u - kNA (one 16-byte read).
   template <int F>
   __device__ __forceinline__ void read_unit(const char* s, int kk, int u) {
-    if (u < 4) {
+    if (u < kNA) {
       const uint32_t b = lds_base + uint32_t(s - smem) + da_of(kk);
       const u32x2 lo = ds_read_tr16(b + a_rd[u][0]);
       const u32x2 hi = ds_read_tr16(b + a_rd[u][1]);
       fa[F][u] = u32x4{lo[0], lo[1], hi[0], hi[1]};
     } else {
-      fb[F][u - 4] =
-          *reinterpret_cast<const u32x4*>(s + (boff ^ uint32_t(kk << 5)) + (u - 4) * 32 * 128);
+      fb[F][u - kNA] =
+          *reinterpret_cast<const u32x4*>(s + (boff ^ uint32_t(kk << 5)) + (u - kNA) * 32 * 128);
     }
   }
 
@@ -181,11 +201,18 @@ struct GemmCoreTr {
   // of the wait, so that no use of them can be placed before it.
   template <int F>
   __device__ __forceinline__ void settle() {
-    asm volatile("s_waitcnt lgkmcnt(0)"
-                 : "+v"(fa[F][0]), "+v"(fa[F][1]), "+v"(fa[F][2]), "+v"(fa[F][3]),
-                   "+v"(fb[F][0]), "+v"(fb[F][1]), "+v"(fb[F][2]), "+v"(fb[F][3])
-                 :
-                 : "memory");
+    if constexpr (kNA == 4)
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[F][0]), "+v"(fa[F][1]), "+v"(fa[F][2]), "+v"(fa[F][3]),
+                     "+v"(fb[F][0]), "+v"(fb[F][1]), "+v"(fb[F][2]), "+v"(fb[F][3])
+                   :
+                   : "memory");
+    else
+      asm volatile("s_waitcnt lgkmcnt(0)"
+                   : "+v"(fa[F][0]), "+v"(fa[F][1]),
+                     "+v"(fb[F][0]), "+v"(fb[F][1]), "+v"(fb[F][2]), "+v"(fb[F][3])
+                   :
+                   : "memory");
     unpack_shift<F>();
   }
 
@@ -223,18 +250,18 @@ struct GemmCoreTr {
   }
 
   // One k-step on set F while reading k-step kk of stage buffer s into set
-  // F^1 (one read unit per MFMA) and, if Load, issuing load pairs
-  // first_pair .. first_pair+3 of stage lkt at MFMAs 0, 4, 8, 12.  A block i
-  // of set F is shifted just before its first MFMA.
+  // F^1 (one read unit per MFMA) and, if Load, issuing a load pair of stage
+  // lkt at every fourth MFMA, from first_pair on.  A block i of set F is
+  // shifted just before its first MFMA.
   template <int F, bool Load>
   __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
 #pragma unroll
-    for (int idx = 0; idx < 16; ++idx) {
+    for (int idx = 0; idx < kNM; ++idx) {
       mfma_one<F>(idx);
-      if (idx < 8) read_unit<F ^ 1>(s, kk, idx);
-      if (idx == 8) read_shift<F ^ 1>(s, kk);
+      if (idx < kNR) read_unit<F ^ 1>(s, kk, idx);
+      if (idx == kNR) read_shift<F ^ 1>(s, kk);
       if (Load && (idx & 3) == 0) load_pair(lkt, first_pair + (idx >> 2));
-      if ((idx & 3) == 3 && idx < 15) shift_frag<F>((idx >> 2) + 1);
+      if ((idx & 3) == 3 && idx < kNM - 1) shift_frag<F>((idx >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
     settle<F ^ 1>();
@@ -252,10 +279,11 @@ struct GemmCoreTr {
     const int lkt = kt + 1;
     if (Load && (lkt & 3) == 0) set_a_tile(lkt >> 2);
     step<0, Load>(s, 1, lkt, 0);
-    step<1, Load>(s, 2, lkt, 4);
+    step<1, Load>(s, 2, lkt, kLPw / 2);
     step<0, false>(s, 3, lkt, 0);
+    constexpr int kHalf = kNM / 2;
 #pragma unroll
-    for (int idx = 0; idx < 8; ++idx) {
+    for (int idx = 0; idx < kHalf; ++idx) {
       mfma_one<1>(idx);
       if ((idx & 3) == 3) shift_frag<1>((idx >> 2) + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -265,11 +293,14 @@ struct GemmCoreTr {
       GemmCore::barrier();
       const char* sn = smem + ((kt + 1) & 1) * kStage;
 #pragma unroll
-      for (int idx = 8; idx < 16; ++idx) {
+      for (int idx = kHalf; idx < kNM; ++idx) {
         mfma_one<1>(idx);
-        read_unit<0>(sn, 0, idx - 8);
-        if (idx == 11) shift_frag<1>(3);
-        if (idx == 12) read_shift<0>(sn, 0);
+        // the next stage's k-step-0 units, spread over the second half
+#pragma unroll
+        for (int u = (idx - kHalf) * kNR / kHalf; u < (idx - kHalf + 1) * kNR / kHalf; ++u)
+          read_unit<0>(sn, 0, u);
+        if ((idx & 3) == 3 && idx < kNM - 1) shift_frag<1>((idx >> 2) + 1);
+        if (idx == kNM - 4) read_shift<0>(sn, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       settle<0>();
@@ -277,9 +308,9 @@ struct GemmCoreTr {
       __builtin_amdgcn_sched_barrier(0);
     } else {
 #pragma unroll
-      for (int idx = 8; idx < 16; ++idx) {
+      for (int idx = kHalf; idx < kNM; ++idx) {
         mfma_one<1>(idx);
-        if (idx == 11) shift_frag<1>(3);
+        if ((idx & 3) == 3 && idx < kNM - 1) shift_frag<1>((idx >> 2) + 1);
       }
     }
   }
@@ -289,11 +320,11 @@ struct GemmCoreTr {
   __device__ __forceinline__ void run(int K) {
     nk = K / 64;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) load_pair(0, u);
+    for (int u = 0; u < kLPw; ++u) load_pair(0, u);
     GemmCore::wait_loads_except(0);
     GemmCore::barrier();
 #pragma unroll
-    for (int u = 0; u < 8; ++u) read_unit<0>(smem, 0, u);
+    for (int u = 0; u < kNR; ++u) read_unit<0>(smem, 0, u);
     read_shift<0>(smem, 0);
     settle<0>();
     shift_frag<0>(0);
@@ -303,5 +334,7 @@ struct GemmCoreTr {
     GemmCore::barrier();
   }
 };
+
+using GemmCoreTr = GemmCoreTrT<4>;
 
 }  // namespace rz

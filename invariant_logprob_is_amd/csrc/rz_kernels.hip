@@ -1160,37 +1160,40 @@ __global__ __launch_bounds__(256) void k_scale_rows_t(const uint16_t* __restrict
   for (int r = ty; r < 64; r += 4) hsT[int64_t(h0 + r) * TCp + t0 + tx] = tile[tx][r];
 }
 
-// The softmax part of dW straight from the stored e (GemmCoreTr): dW[v][h] =
+// The softmax part of dW straight from the stored e (GemmCoreTrT): dW[v][h] =
 // (first ? 0 : dW[v][h]) - sum_t (e_tv 2^-d(t, vt)) hsT[h][t].
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+constexpr int kDwWaves = 8;
+using DwCore = GemmCoreTrT<kDwWaves>;
+
+__global__ __launch_bounds__(64 * kDwWaves)
+__attribute__((amdgpu_waves_per_eu(kDwWaves / 4, kDwWaves / 4)))
 void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int64_t ds,
              const uint16_t* __restrict__ hsT, int64_t TCp, int H, int V, int64_t Vp,
              int64_t n_vt, int64_t n_ht, int first, float* __restrict__ dW) {
-  __shared__ __attribute__((aligned(16))) char lds[GemmCoreTr::kRing];
+  __shared__ __attribute__((aligned(16))) char lds[DwCore::kRing];
   int64_t vt, ht;
   if (!tile_of(n_vt, n_ht, vt, ht)) return;
   const int64_t v0 = vt * kTile;
   const int64_t h0 = ht * kTile;
-  GemmCoreTr g;
+  DwCore g;
   g.init(E, Vp / 16, vt, hsT, H, ht, D + vt * ds, TCp, lds);
   g.run(int(TCp));
-  f32x16 (&acc)[4][4] = g.acc;
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int wm = wave & 1;
-  const int wn = wave >> 1;
+  const int wm = wave % DwCore::kWM;
+  const int wn = wave / DwCore::kWM;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < DwCore::kNA; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t v = v0 + acc_row(wm, i, r, lane);
+      const int64_t v = v0 + acc_row(wm, i, r, lane, DwCore::kNA);
       if (v >= V) continue;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t h = h0 + acc_col(wn, j, lane);
+      for (int j = 0; j < DwCore::kNB; ++j) {
+        const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
         if (h < H) {
           float* o = dW + v * H + h;
-          *o = (first ? 0.0f : *o) - acc[i][j][r];
+          *o = (first ? 0.0f : *o) - g.acc[i][j][r];
         }
       }
     }
@@ -1472,7 +1475,7 @@ hipError_t launch_weight_grads_chunk(const uint16_t* E, const uint32_t* D, int64
                        coef_chunk, g, TC, TCp, H, hs);
     const int64_t n_vt = n_vocab_tiles(V);
     const int64_t n_ht = ceil_div(H, kTile);
-    hipLaunchKernelGGL(k_dw_tr, dim3(raster_grid(n_vt * n_ht)), dim3(kThreads), 0, s, E, D, ds,
+    hipLaunchKernelGGL(k_dw_tr, dim3(raster_grid(n_vt * n_ht)), dim3(64 * kDwWaves), 0, s, E, D, ds,
                        hs, TCp, H, V, Vp, n_vt, n_ht, first, dW);
   }
   hipError_t e = hipGetLastError();
