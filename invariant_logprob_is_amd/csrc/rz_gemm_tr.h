@@ -297,10 +297,11 @@ struct GemmCoreTrT {
         mfma_one<1>(idx);
         // the next stage's k-step-0 units, spread over the second half
 #pragma unroll
-        for (int u = (idx - kHalf) * kNR / kHalf; u < (idx - kHalf + 1) * kNR / kHalf; ++u)
+        for (int u = (idx - kHalf) * kNR / (kNM - kHalf); u < (idx - kHalf + 1) * kNR / (kNM - kHalf);
+             ++u)
           read_unit<0>(sn, 0, u);
         if ((idx & 3) == 3 && idx < kNM - 1) shift_frag<1>((idx >> 2) + 1);
-        if (idx == kNM - 4) read_shift<0>(sn, 0);
+        if (idx == (kHalf > kNM - 4 ? kHalf : kNM - 4)) read_shift<0>(sn, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
       settle<0>();

@@ -813,22 +813,46 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
   const int wave = threadIdx.x >> 6;
   const int wm = Core::wave_m(wave);
   const int wn = Core::wave_n(wave);
+  // Four rows at a time: their targets, scales and target-row weights are all
+  // loaded before the first is used, so the loads are in flight together
+  // instead of one round trip per output.
 #pragma unroll
   for (int i = 0; i < Core::kNA; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t t = t0 + acc_row(wm, i, r, lane, Core::kNA);
-      if (t >= TC) continue;
-      const int64_t tg = target[t];
-      const float c = coef[t];
-      const float gt = gf[t];
-      const bool ok = tg >= 0 && tg < V;
+    for (int rq = 0; rq < 4; ++rq) {
+      int64_t t[4];
+      int32_t tg[4];
+      float c[4], gt[4];
 #pragma unroll
-      for (int j = 0; j < Core::kNB; ++j) {
-        const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
-        if (h < H) {
-          const float wt = ok ? bf16_to_f32(W[tg * H + h]) : NAN;
-          dh[t * H + h] = c * (wt - gt * acc[i][j][r]);
+      // (addresses are clamped to the tile's first row and column, which
+      // exist, so the loads need no branch that would hold them apart)
+      for (int u = 0; u < 4; ++u) {
+        t[u] = t0 + acc_row(wm, i, rq * 4 + u, lane, Core::kNA);
+        const int64_t tl = t[u] < TC ? t[u] : t0;
+        tg[u] = target[tl];
+        c[u] = coef[tl];
+        gt[u] = gf[tl];
+      }
+      uint16_t w[4][Core::kNB];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+#pragma unroll
+        for (int j = 0; j < Core::kNB; ++j) {
+          const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
+          const bool ok = tg[u] >= 0 && tg[u] < V && h < H;
+          w[u][j] = W[ok ? int64_t(tg[u]) * H + h : int64_t(0)];
+        }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (t[u] >= TC) continue;
+        const bool ok = tg[u] >= 0 && tg[u] < V;
+#pragma unroll
+        for (int j = 0; j < Core::kNB; ++j) {
+          const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
+          if (h < H) {
+            const float wt = ok ? bf16_to_f32(w[u][j]) : NAN;
+            dh[t[u] * H + h] = c[u] * (wt - gt[u] * acc[i][j][rq * 4 + u]);
+          }
         }
       }
     }
@@ -1182,18 +1206,32 @@ void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int
   const int wave = threadIdx.x >> 6;
   const int wm = wave % DwCore::kWM;
   const int wn = wave / DwCore::kWM;
+  // Four rows at a time: the previous chunks' sums of the quad are all
+  // loaded before the first store, so the loads are in flight together (the
+  // first chunk loads and ignores them; clamped addresses need no branch).
 #pragma unroll
   for (int i = 0; i < DwCore::kNA; ++i) {
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int64_t v = v0 + acc_row(wm, i, r, lane, DwCore::kNA);
-      if (v >= V) continue;
+    for (int rq = 0; rq < 4; ++rq) {
+      float old[4][DwCore::kNB];
 #pragma unroll
-      for (int j = 0; j < DwCore::kNB; ++j) {
-        const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
-        if (h < H) {
-          float* o = dW + v * H + h;
-          *o = (first ? 0.0f : *o) - g.acc[i][j][r];
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + acc_row(wm, i, rq * 4 + u, lane, DwCore::kNA);
+#pragma unroll
+        for (int j = 0; j < DwCore::kNB; ++j) {
+          const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
+          const float o = dW[(v < V && h < H) ? v * H + h : v0 * H + h0];
+          old[u][j] = first ? 0.0f : o;
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int64_t v = v0 + acc_row(wm, i, rq * 4 + u, lane, DwCore::kNA);
+        if (v >= V) continue;
+#pragma unroll
+        for (int j = 0; j < DwCore::kNB; ++j) {
+          const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
+          if (h < H) dW[v * H + h] = old[u][j] - g.acc[i][j][rq * 4 + u];
         }
       }
     }
