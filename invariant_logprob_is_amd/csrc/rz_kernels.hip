@@ -787,6 +787,8 @@ __global__ __launch_bounds__(256) void k_transpose_w(const uint16_t* __restrict_
 // fragments (token rows) per step carry the exponent shift, half as many as
 // in a 128-row sub-tile.
 constexpr int kDhWaves = 8;
+// Rows of an accumulator block whose epilogue loads are issued together.
+constexpr int kEpiRows = 4;
 constexpr int kDhABlocks = 2;
 constexpr int kDhPipe = 2;   // the deep A ring: e is streamed from HBM
 
@@ -813,29 +815,29 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
   const int wave = threadIdx.x >> 6;
   const int wm = Core::wave_m(wave);
   const int wn = Core::wave_n(wave);
-  // Four rows at a time: their targets, scales and target-row weights are all
+  // kEpiRows rows at a time: their targets, scales and target-row weights are all
   // loaded before the first is used, so the loads are in flight together
   // instead of one round trip per output.
 #pragma unroll
   for (int i = 0; i < Core::kNA; ++i) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      int64_t t[4];
-      int32_t tg[4];
-      float c[4], gt[4];
+    for (int rq = 0; rq < 16 / kEpiRows; ++rq) {
+      int64_t t[kEpiRows];
+      int32_t tg[kEpiRows];
+      float c[kEpiRows], gt[kEpiRows];
 #pragma unroll
       // (addresses are clamped to the tile's first row and column, which
       // exist, so the loads need no branch that would hold them apart)
-      for (int u = 0; u < 4; ++u) {
-        t[u] = t0 + acc_row(wm, i, rq * 4 + u, lane, Core::kNA);
+      for (int u = 0; u < kEpiRows; ++u) {
+        t[u] = t0 + acc_row(wm, i, rq * kEpiRows + u, lane, Core::kNA);
         const int64_t tl = t[u] < TC ? t[u] : t0;
         tg[u] = target[tl];
         c[u] = coef[tl];
         gt[u] = gf[tl];
       }
-      uint16_t w[4][Core::kNB];
+      uint16_t w[kEpiRows][Core::kNB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kEpiRows; ++u)
 #pragma unroll
         for (int j = 0; j < Core::kNB; ++j) {
           const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
@@ -843,7 +845,7 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
           w[u][j] = W[ok ? int64_t(tg[u]) * H + h : int64_t(0)];
         }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
+      for (int u = 0; u < kEpiRows; ++u) {
         if (t[u] >= TC) continue;
         const bool ok = tg[u] >= 0 && tg[u] < V;
 #pragma unroll
@@ -851,7 +853,7 @@ void k_dhidden(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, i
           const int64_t h = h0 + acc_col(wn, j, lane, Core::kNB);
           if (h < H) {
             const float wt = ok ? bf16_to_f32(w[u][j]) : NAN;
-            dh[t[u] * H + h] = c[u] * (wt - gt[u] * acc[i][j][rq * 4 + u]);
+            dh[t[u] * H + h] = c[u] * (wt - gt[u] * acc[i][j][rq * kEpiRows + u]);
           }
         }
       }
@@ -1206,17 +1208,17 @@ void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int
   const int wave = threadIdx.x >> 6;
   const int wm = wave % DwCore::kWM;
   const int wn = wave / DwCore::kWM;
-  // Four rows at a time: the previous chunks' sums of the quad are all
+  // kEpiRows rows at a time: the previous chunks' sums of those rows are all
   // loaded before the first store, so the loads are in flight together (the
   // first chunk loads and ignores them; clamped addresses need no branch).
 #pragma unroll
   for (int i = 0; i < DwCore::kNA; ++i) {
 #pragma unroll
-    for (int rq = 0; rq < 4; ++rq) {
-      float old[4][DwCore::kNB];
+    for (int rq = 0; rq < 16 / kEpiRows; ++rq) {
+      float old[kEpiRows][DwCore::kNB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t v = v0 + acc_row(wm, i, rq * 4 + u, lane, DwCore::kNA);
+      for (int u = 0; u < kEpiRows; ++u) {
+        const int64_t v = v0 + acc_row(wm, i, rq * kEpiRows + u, lane, DwCore::kNA);
 #pragma unroll
         for (int j = 0; j < DwCore::kNB; ++j) {
           const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
@@ -1225,13 +1227,13 @@ void k_dw_tr(const uint16_t* __restrict__ E, const uint32_t* __restrict__ D, int
         }
       }
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int64_t v = v0 + acc_row(wm, i, rq * 4 + u, lane, DwCore::kNA);
+      for (int u = 0; u < kEpiRows; ++u) {
+        const int64_t v = v0 + acc_row(wm, i, rq * kEpiRows + u, lane, DwCore::kNA);
         if (v >= V) continue;
 #pragma unroll
         for (int j = 0; j < DwCore::kNB; ++j) {
           const int64_t h = h0 + acc_col(wn, j, lane, DwCore::kNB);
-          if (h < H) dW[v * H + h] = old[u][j] - g.acc[i][j][rq * 4 + u];
+          if (h < H) dW[v * H + h] = old[u][j] - g.acc[i][j][rq * kEpiRows + u];
         }
       }
     }
