@@ -39,16 +39,21 @@
  *     detected on the device and yield NaN for the loss and every coef.
  *   - Determinism: outputs are bitwise identical run to run.  Every
  *     floating-point sum runs in a fixed order; the only atomics are integer
- *     counts (the digit histograms of the weight gradient's bucketing),
- *     whose totals do not depend on the order, and each entry's place in a
- *     bucket is fixed by its token index, not by arrival.
+ *     counters: the forward's per-XCD tile counters, which decide which
+ *     workgroup computes a tile but never how it is computed, and the digit
+ *     histograms of the weight gradient's bucketing, whose totals do not
+ *     depend on the order (each entry's place in a bucket is fixed by its
+ *     token index, not by arrival).
  *   - Layout: row t pairs the final hidden state that predicts target[t] with
  *     that target (the caller applies the next-token shift and drops prompt
  *     tokens).  Tokens of a response are contiguous; the responses of one
  *     prompt group are contiguous.
  *   - Thread safety: no global mutable state apart from the opt-in timing
- *     records of rz_profile_* (process-wide, behind a lock); concurrent
- *     calls are safe if they use distinct workspaces and outputs.
+ *     records of rz_profile_* (process-wide, behind a lock), per-device
+ *     values looked up once (the CU count; the address of
+ *     rz_logprob_noalloc's scratch) and that scratch itself; concurrent
+ *     calls are safe if they use distinct workspaces and outputs (for
+ *     rz_logprob_noalloc, see there).
  */
 #ifndef RZ_H_
 #define RZ_H_
