@@ -432,6 +432,80 @@ def shards(args, b, rz, x, g, W, tgt, lp, lse, ws):
     }), flush=True)
 
 
+def stored(args, b, rz, x, g, W, tgt, mu, ro, go, reward, ws, outs):
+    """The learner head through the separate entry points with stored logits:
+    rz_logprob_store, rz_is_loss, rz_backward_stored.  The whole batch's
+    logits stay in HBM between the forward and the backward (about 2 bytes
+    per logit); the bits are checked against rz_learner_step's."""
+    import torch
+
+    dev = x.device
+    T, H, V = b.T, b.H, b.V
+    need = rz.logits_bytes(T, H, V)
+    free, _ = torch.cuda.mem_get_info(dev)
+    if need + (1 << 30) > free:
+        raise SystemExit(f"stored logits need {need / 2**30:.1f} GiB, {free / 2**30:.1f} GiB free")
+    buf = torch.empty(need, dtype=torch.uint8, device=dev)
+    lp = torch.empty(T, dtype=torch.float32, device=dev)
+    lse = torch.empty(T, dtype=torch.float32, device=dev)
+    dh = torch.empty(T, H, dtype=torch.float32, device=dev)
+    log(f"stored logits {need / 2**30:.1f} GiB")
+    res = {}
+
+    def call():
+        rz.logprob_store(x, g, W, tgt, b.eps, logits=buf, workspace=ws, out=lp, lse_out=lse)
+        res["loss"], res["coef"], _ = rz.is_loss(lp, mu, ro, go, reward, workspace=ws,
+                                                 want_advantage=False)
+        rz.backward_stored(x, g, W, tgt, lse, res["coef"], buf, b.eps, workspace=ws, out=dh)
+
+    rz.learner_step(x, g, W, tgt, mu, ro, go, reward, b.eps, workspace=ws, out=outs)
+    for _ in range(args.warmup):
+        call()
+    torch.cuda.synchronize()
+    same = all(torch.equal(a.view(torch.int32), c.view(torch.int32))
+               for a, c in ((lp, outs["logprob"]), (res["coef"], outs["coef"]),
+                            (dh, outs["dhidden"])))
+    same = same and bool(torch.equal(res["loss"], outs["loss"]))
+    rz.profile_enable(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        call()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    prof = rz.profile_read()
+    rz.profile_enable(False)
+    ms = 1000.0 * wall / args.steps
+    log(f"stored-logits pass {ms:.2f} ms; bits equal to rz_learner_step: {same}")
+    for k, (tot, n) in sorted(prof.items(), key=lambda kv: -kv[1][0]):
+        log(f"  {k:16s} {tot / args.steps:9.3f} ms/pass  {n // args.steps:4d} launches/pass")
+    if not same:
+        raise SystemExit("stored-logits pass differs from rz_learner_step")
+    kernels = {}
+    for k in ("k_lmhead_fwd", "k_dhidden"):
+        tot, n = prof[k]
+        achieved = 2.0 * T * H * V * args.steps / (tot / 1000.0)
+        kernels[k] = {"ms_per_step": tot / args.steps, "achieved_tflops": achieved / 1e12,
+                      "frac": achieved / PEAK_BF16_FLOPS}
+    dom = max(kernels, key=lambda k: kernels[k]["ms_per_step"])
+    tps = T / (ms / 1000.0)
+    print(json.dumps({
+        "metric": "stored-logits learner tokens/sec (rz_logprob_store + rz_is_loss + "
+                  "rz_backward_stored) and % bf16 MFMA peak, 1 GPU",
+        "value": tps, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": f"{b.name}: T={T} tokens, H={H}, V={V}, {b.R} responses in "
+                               f"{b.G} groups; logits stored between the calls",
+                   "T": T, "H": H, "V": V, "R": b.R, "G": b.G, "stored_logits_bytes": need},
+        "mfma_frac_algorithmic": tps * 4.0 * H * V / PEAK_BF16_FLOPS,
+        "bits_equal_rz_learner_step": same, "kernels": kernels,
+        "roofline": {"kernel": dom, "bound": "mfma", "achieved": kernels[dom]["achieved_tflops"],
+                     "peak": PEAK_BF16_FLOPS / 1e12, "unit": "TFLOP/s",
+                     "frac": kernels[dom]["frac"], "traffic": None},
+    }), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -450,6 +524,10 @@ def main():
     ap.add_argument("--shards", type=int, choices=[1, 2, 4, 8],
                     help="time the log-probabilities through this many equal shares of the "
                          "vocabulary splits and their merge instead of the learner step")
+    ap.add_argument("--stored", action="store_true",
+                    help="time the separate entry points with the whole batch's logits stored "
+                         "between forward and backward (rz_logprob_store, rz_is_loss, "
+                         "rz_backward_stored) instead of the learner step")
     ap.add_argument("--summarize-counters", nargs="+", metavar="CSV",
                     help="turn rocprofv3 --pmc runs of this script (FETCH_SIZE, WRITE_SIZE and "
                          "optionally TCC_EA0_RDREQ_DRAM_sum + TCC_EA0_WRREQ_DRAM_sum) into "
@@ -457,6 +535,9 @@ def main():
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0 or args.cpu_tokens < 1:
         ap.error("--steps and --cpu-tokens must be at least 1, --warmup at least 0")
+    if sum(map(bool, (args.probe, args.shards, args.stored))) > 1 or (
+            args.grads and (args.probe or args.shards or args.stored)):
+        ap.error("--probe, --shards and --stored each time their own pass, without --grads")
     if args.summarize_counters:
         if len(args.summarize_counters) not in (2, 3):
             ap.error("--summarize-counters takes FETCH_CSV WRITE_CSV [DRAM_CSV]")
@@ -517,6 +598,9 @@ def main():
         return
     if args.shards:
         shards(args, b, rz, x, g, W, tgt, lp, lse, ws)
+        return
+    if args.stored:
+        stored(args, b, rz, x, g, W, tgt, mu, ro, go, reward, ws, outs)
         return
 
     def step():

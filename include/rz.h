@@ -364,6 +364,55 @@ RZ_API int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps,
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * Stored logits (the same gradient of the loss, [P2] "Alignment permits a
+ * simpler learning path"; the same forward, [P3] body): rz_logprob_store is
+ * rz_logprob that also keeps, in a caller-owned buffer `logits`, what
+ * rz_backward needs from the forward --
+ * the values e of every logit (bf16, relative to their vocabulary tile's
+ * integer reference), the tile maxima and the target logits -- and
+ * rz_backward_stored is rz_backward that takes them from there instead of
+ * recomputing the logits: 2 H V flops per token instead of 4 for the two
+ * calls after the forward.  Each e is relative to its tile's own reference,
+ * which is known as soon as the tile is computed, so the forward can store
+ * it before the row's log-sum-exp exists; the backward turns e into the
+ * probabilities with exponent shifts it derives from lse.  The buffer takes
+ * about T * V * 2 bytes (181 GB, 168 GiB, at T = 584,025, V = 151,936):
+ * the caller decides whether that fits beside everything else.
+ *
+ * rz_logits_bytes -- size of `logits` for these sizes; 0 if invalid.  Host
+ * only, no HIP call.
+ */
+RZ_API size_t rz_logits_bytes(int64_t T, int32_t H, int32_t V);
+
+/*
+ * rz_logprob_store -- rz_logprob (same arguments, same logprob and lse bits)
+ * that also fills `logits` (device memory, 256-byte aligned, at least
+ * rz_logits_bytes(T, H, V) bytes, owned by the caller; RZ_EWORKSPACE if
+ * smaller).  Its contents are only meaningful to rz_backward_stored with the
+ * same x, gamma, eps, W, target and sizes.
+ */
+RZ_API int rz_logprob_store(const uint16_t* x, const uint16_t* gamma, float eps,
+                const uint16_t* W, const int32_t* target,
+                int64_t T, int32_t H, int32_t V,
+                float* logprob, float* lse,
+                void* logits, size_t logits_bytes,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * rz_backward_stored -- rz_backward (same arguments) with the logits that
+ * rz_logprob_store kept for the same inputs: its dhidden is bit-identical
+ * to rz_backward's.  Errors: as rz_backward; RZ_EWORKSPACE if logits_bytes
+ * is below rz_logits_bytes(T, H, V).
+ */
+RZ_API int rz_backward_stored(const uint16_t* x, const uint16_t* gamma, float eps,
+                const uint16_t* W, const int32_t* target,
+                const float* lse, const float* coef,
+                int64_t T, int32_t H, int32_t V,
+                const void* logits, size_t logits_bytes,
+                float* dhidden,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rz_learner_step -- the whole learner head for one update in one call:
  * rz_logprob, rz_is_loss, rz_d3 and the gradient to the hidden states, with
  * the log-probabilities bit-identical to rz_logprob's.

@@ -56,6 +56,11 @@ SYMBOLS = {
     "rz_is_loss": (ctypes.c_int, [_P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P, _P, _P, _SZ, _P]),
     "rz_d3": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_backward": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _P, _SZ, _P]),
+    "rz_logits_bytes": (_SZ, [_I64, _I32, _I32]),
+    "rz_logprob_store": (ctypes.c_int, [_P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P, _P, _SZ,
+                                        _P, _SZ, _P]),
+    "rz_backward_stored": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P,
+                                          _SZ, _P, _P, _SZ, _P]),
     "rz_kl": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_decompose": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P,
                                     _P, _P, _SZ, _P]),
@@ -459,6 +464,69 @@ def backward(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, workspace=Non
                            target.data_ptr(), lse.data_ptr(), coef.data_ptr(), T, H, V,
                            dh.data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
     _check("rz_backward", st)
+    return dh
+
+
+def logits_bytes(T: int, H: int, V: int) -> int:
+    """rz_logits_bytes: size of the stored-logits buffer of logprob_store()."""
+    return int(lib().rz_logits_bytes(T, H, V))
+
+
+def logprob_store(x, gamma, W, target, eps: float = 1e-6, *, logits=None, workspace=None,
+                  out=None, lse_out=None):
+    """logprob() that also keeps the logits for backward_stored()
+    (rz_logprob_store).  Returns (logprob, lse, logits); `logits` is a uint8
+    device buffer of logits_bytes(T, H, V) bytes (allocated if not given)."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    V = W.shape[0]
+    if gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T:
+        raise ValueError("shape mismatch among x, gamma, W, target")
+    lp = out if out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    ls = lse_out if lse_out is not None else torch.empty(T, dtype=torch.float32, device=dev)
+    _need(lp, "out", torch.float32, dev, 1)
+    _need(ls, "lse_out", torch.float32, dev, 1)
+    lg = _workspace(logits_bytes(T, H, V), dev, logits)
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    st = lib().rz_logprob_store(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                                target.data_ptr(), T, H, V, lp.data_ptr(), ls.data_ptr(),
+                                lg.data_ptr(), lg.numel(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_logprob_store", st)
+    return lp, ls, lg
+
+
+def backward_stored(x, gamma, W, target, lse, coef, logits, eps: float = 1e-6, *, workspace=None,
+                    out=None):
+    """backward() from the logits that logprob_store() kept for the same
+    inputs (rz_backward_stored): the same dhidden bits, without recomputing
+    the logits."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    _need(lse, "lse", torch.float32, dev, 1)
+    _need(coef, "coef", torch.float32, dev, 1)
+    _need(logits, "logits", torch.uint8, dev, 1)
+    V = W.shape[0]
+    if (gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T or lse.shape[0] != T
+            or coef.shape[0] != T):
+        raise ValueError("shape mismatch among backward arguments")
+    dh = out if out is not None else torch.empty(T, H, dtype=torch.float32, device=dev)
+    _need(dh, "out", torch.float32, dev, 2)
+    ws = _workspace(workspace_bytes(T, H, V), dev, workspace)
+    st = lib().rz_backward_stored(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                                  target.data_ptr(), lse.data_ptr(), coef.data_ptr(), T, H, V,
+                                  logits.data_ptr(), logits.numel(), dh.data_ptr(), ws.data_ptr(),
+                                  ws.numel(), _stream(dev))
+    _check("rz_backward_stored", st)
     return dh
 
 

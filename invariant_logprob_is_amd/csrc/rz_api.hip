@@ -125,6 +125,73 @@ hipError_t scratch_on_current_device(void** out) {
   return hipSuccess;
 }
 
+// Argument checks shared by rz_backward and rz_backward_stored.
+int check_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                   const int32_t* target, const float* lse, const float* coef, int64_t T,
+                   int32_t H, int32_t V, float* dhidden, void* workspace,
+                   size_t workspace_bytes) {
+  if (!x || !gamma || !W || !target || !lse || !coef || !dhidden || !workspace) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) || !aligned4(lse) ||
+      !aligned4(coef) || !aligned16(dhidden) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return RZ_EINVAL;
+  if (!(eps >= 0.0f)) return RZ_EINVAL;
+  const int st = check_head_shape(T, H, V);
+  if (st != RZ_OK) return st;
+  if (workspace_bytes < ws_layout(T, H, V).total) return RZ_EWORKSPACE;
+  return RZ_OK;
+}
+
+// rz_backward, and rz_backward_stored (stored != nullptr): per chunk, the
+// forward with the e store (its (m, S, z_target) partials are recomputed
+// and left unused) or the stored chunk, the shift table from the given lse,
+// then the same contraction the learner step runs.
+hipError_t run_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                        const int32_t* target, const float* lse, const float* coef, int64_t T,
+                        int32_t H, int32_t V, const char* stored, float* dhidden,
+                        void* workspace, hipStream_t s) {
+  const WsLayout L = ws_layout(T, H, V);
+  const StoredLayout SL = stored_layout(T, V);
+  uint16_t* hh = at<uint16_t>(workspace, L.b_hhat);
+  uint16_t* Wt = at<uint16_t>(workspace, L.b_wt);
+  uint32_t* D = at<uint32_t>(workspace, L.b_d);
+  float* g = at<float>(workspace, L.b_g);
+  SelRec* rec = at<SelRec>(workspace, L.b_rec);
+  hipError_t e = launch_transpose_w(W, H, V, Wt, s);
+  for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
+    const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
+    const int64_t ds = shift_stride(tc);
+    const uint16_t* E;
+    const float* pm;
+    const float* zt;
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
+    if (stored) {
+      const char* c = stored + size_t(c0 / kBwdChunk) * SL.stride;
+      E = reinterpret_cast<const uint16_t*>(c + SL.e);
+      pm = reinterpret_cast<const float*>(c + SL.pm);
+      zt = reinterpret_cast<const float*>(c + SL.zt);
+    } else {
+      uint16_t* Ew = at<uint16_t>(workspace, L.b_e);
+      float* pmw = at<float>(workspace, L.b_pm);
+      float* ztw = at<float>(workspace, L.b_zt);
+      if (e == hipSuccess)
+        e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pmw, at<float>(workspace, L.b_ps), ztw,
+                              Ew, at<int>(workspace, L.b_tick), s);
+      E = Ew;
+      pm = pmw;
+      zt = ztw;
+    }
+    if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
+    if (e == hipSuccess)
+      e = launch_select(pm, tc, V, lse + c0, zt, target + c0, coef + c0, D, ds, g, E, hh, W, H,
+                        rec, s);
+    if (e == hipSuccess)
+      e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
+    if (e == hipSuccess) e = launch_dh_fix(rec, coef + c0, W, tc, H, dhidden + c0 * H, s);
+    if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
+  }
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
@@ -348,50 +415,77 @@ int rz_decompose(const uint16_t* x_new, const uint16_t* gamma_new, const uint16_
 int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
                 const int32_t* target, const float* lse, const float* coef, int64_t T, int32_t H,
                 int32_t V, float* dhidden, void* workspace, size_t workspace_bytes, void* stream) {
-  if (!x || !gamma || !W || !target || !lse || !coef || !dhidden || !workspace) return RZ_EINVAL;
-  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) || !aligned4(lse) ||
-      !aligned4(coef) || !aligned16(dhidden) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
+  int st = check_backward(x, gamma, eps, W, target, lse, coef, T, H, V, dhidden, workspace,
+                          workspace_bytes);
+  if (st != RZ_OK) return st;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  return status_of(run_backward(x, gamma, eps, W, target, lse, coef, T, H, V, nullptr, dhidden,
+                                workspace, static_cast<hipStream_t>(stream)));
+}
+
+size_t rz_logits_bytes(int64_t T, int32_t H, int32_t V) {
+  if (T < 1 || H < 1 || V < 1) return 0;
+  return stored_layout(T, V).total;
+}
+
+int rz_logprob_store(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                     const int32_t* target, int64_t T, int32_t H, int32_t V, float* logprob,
+                     float* lse, void* logits, size_t logits_bytes, void* workspace,
+                     size_t workspace_bytes, void* stream) {
+  if (!x || !gamma || !W || !target || !logprob || !logits || !workspace) return RZ_EINVAL;
+  if (!aligned16(x) || !aligned16(gamma) || !aligned16(W) || !aligned4(target) ||
+      !aligned4(logprob) || (lse && !aligned4(lse)) ||
+      (reinterpret_cast<uintptr_t>(logits) & 255u) || (reinterpret_cast<uintptr_t>(workspace) & 255u))
     return RZ_EINVAL;
   if (!(eps >= 0.0f)) return RZ_EINVAL;
   int st = check_head_shape(T, H, V);
   if (st != RZ_OK) return st;
   const WsLayout L = ws_layout(T, H, V);
-  if (workspace_bytes < L.total) return RZ_EWORKSPACE;
+  const StoredLayout SL = stored_layout(T, V);
+  if (workspace_bytes < L.total || logits_bytes < SL.total) return RZ_EWORKSPACE;
   st = check_device();
   if (st != RZ_OK) return st;
 
-  // Per chunk: the forward with the e store (its (m, S, z_target) partials
-  // are recomputed and left unused), the shift table from the given lse, then
-  // the same contraction the learner step runs.
+  // rz_logprob's chunks, with the e store and the partials in `logits`
   hipStream_t s = static_cast<hipStream_t>(stream);
-  uint16_t* hh = at<uint16_t>(workspace, L.b_hhat);
-  uint16_t* Wt = at<uint16_t>(workspace, L.b_wt);
-  uint16_t* E = at<uint16_t>(workspace, L.b_e);
-  float* pm = at<float>(workspace, L.b_pm);
-  float* ps = at<float>(workspace, L.b_ps);
-  float* zt = at<float>(workspace, L.b_zt);
-  uint32_t* D = at<uint32_t>(workspace, L.b_d);
-  float* g = at<float>(workspace, L.b_g);
-  SelRec* rec = at<SelRec>(workspace, L.b_rec);
-  hipError_t e = launch_transpose_w(W, H, V, Wt, s);
+  uint16_t* hhat = at<uint16_t>(workspace, L.hhat);
+  float* ps = at<float>(workspace, L.ps);
+  int* tick = at<int>(workspace, L.tick);
+  hipError_t e = hipSuccess;
   for (int64_t c0 = 0; c0 < T && e == hipSuccess; c0 += kBwdChunk) {
     const int64_t tc = (T - c0 < kBwdChunk) ? T - c0 : kBwdChunk;
-    const int64_t ds = shift_stride(tc);
-    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hh, nullptr, s);
+    char* c = static_cast<char*>(logits) + size_t(c0 / kBwdChunk) * SL.stride;
+    float* pm = reinterpret_cast<float*>(c + SL.pm);
+    float* zt = reinterpret_cast<float*>(c + SL.zt);
+    e = launch_rmsnorm_fwd(x + c0 * H, gamma, eps, tc, H, hhat, nullptr, s);
     if (e == hipSuccess)
-      e = launch_lmhead_fwd(hh, W, target + c0, tc, H, V, pm, ps, zt, E,
-                            at<int>(workspace, L.b_tick), s);
-    if (e == hipSuccess) e = launch_shift_prep(pm, lse + c0, tc, V, D, ds, g, s);
+      e = launch_lmhead_fwd(hhat, W, target + c0, tc, H, V, pm, ps, zt,
+                            reinterpret_cast<uint16_t*>(c + SL.e), tick, s);
     if (e == hipSuccess)
-      e = launch_select(pm, tc, V, lse + c0, zt, target + c0, coef + c0, D, ds, g, E, hh, W, H,
-                        rec, s);
-    if (e == hipSuccess)
-      e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
-    if (e == hipSuccess) e = launch_dh_fix(rec, coef + c0, W, tc, H, dhidden + c0 * H, s);
-    if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
+      e = launch_lse_combine(pm, ps, zt, tc, V, logprob + c0, lse ? lse + c0 : nullptr, nullptr,
+                             nullptr, nullptr, nullptr, 0, nullptr, s);
   }
   return status_of(e);
 }
+
+int rz_backward_stored(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                       const int32_t* target, const float* lse, const float* coef, int64_t T,
+                       int32_t H, int32_t V, const void* logits, size_t logits_bytes,
+                       float* dhidden, void* workspace, size_t workspace_bytes, void* stream) {
+  int st = check_backward(x, gamma, eps, W, target, lse, coef, T, H, V, dhidden, workspace,
+                          workspace_bytes);
+  if (st != RZ_OK) return st;
+  if (!logits || (reinterpret_cast<uintptr_t>(logits) & 255u)) return RZ_EINVAL;
+  if (logits_bytes < stored_layout(T, V).total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  return status_of(run_backward(x, gamma, eps, W, target, lse, coef, T, H, V,
+                                static_cast<const char*>(logits), dhidden, workspace,
+                                static_cast<hipStream_t>(stream)));
+}
+
+
 
 int rz_learner_step(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
                     const int32_t* target, const float* rollout_logprob, int64_t T, int32_t H,

@@ -180,6 +180,27 @@ inline WsLayout ws_layout(int64_t T, int64_t H, int64_t V) {
   return L;
 }
 
+// Stored logits (rz_logprob_store / rz_backward_stored): chunk c of at most
+// kBwdChunk tokens at byte c * stride holds its e block (fragment order, as
+// the forward writes it), its tile maxima pm [n_vt][tc] and its target
+// logits [tc].
+struct StoredLayout {
+  size_t e, pm, zt, stride, total;
+};
+
+inline StoredLayout stored_layout(int64_t T, int64_t V) {
+  StoredLayout S{};
+  const int64_t tc = T < kBwdChunk ? T : kBwdChunk;
+  const int64_t tcp = shift_stride(tc);
+  size_t o = 0;
+  S.e = o;   o = align256(o + size_t(tcp) * vocab_pad(V) * 2);
+  S.pm = o;  o = align256(o + size_t(n_vocab_tiles(V)) * tc * 4);
+  S.zt = o;  o = align256(o + size_t(tc) * 4);
+  S.stride = o;
+  S.total = size_t(ceil_div(T, kBwdChunk)) * S.stride;
+  return S;
+}
+
 // ---------------------------------------------------------------------------
 // Optional per-kernel timing (rz_profile.hip).  While enabled, a ProfScope
 // records a hipEvent on the launch stream before and after the launches in

@@ -98,6 +98,24 @@ def _backward(**kw):
                                 a["stream"])
 
 
+def _logprob_store(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, T=300, H=128, V=1024,
+             logprob=FAKE, lse=FAKE, logits=FAKE, lgb=1 << 40, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_logprob_store(a["x"], a["gamma"], a["eps"], a["W"], a["target"], a["T"],
+                                     a["H"], a["V"], a["logprob"], a["lse"], a["logits"], a["lgb"],
+                                     a["ws"], a["wsb"], a["stream"])
+
+
+def _backward_stored(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, lse=FAKE, coef=FAKE, T=300,
+             H=128, V=1024, logits=FAKE, lgb=1 << 40, dh=FAKE, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return rz.lib().rz_backward_stored(a["x"], a["gamma"], a["eps"], a["W"], a["target"],
+                                       a["lse"], a["coef"], a["T"], a["H"], a["V"], a["logits"],
+                                       a["lgb"], a["dh"], a["ws"], a["wsb"], a["stream"])
+
+
 def _rmsnorm(**kw):
     a = dict(x=FAKE, gamma=FAKE, eps=1e-6, T=300, H=128, hhat=FAKE, rstd=FAKE, stream=None)
     a.update(kw)
@@ -120,7 +138,7 @@ def test_rmsnorm_argument_validation():
     assert _rmsnorm(H=16384 + 64) == rz.RZ_EUNSUPPORTED
 
 
-@pytest.mark.parametrize("fn", [_logprob, _backward])
+@pytest.mark.parametrize("fn", [_logprob, _backward, _logprob_store, _backward_stored])
 def test_head_argument_validation(fn):
     for k in ("x", "gamma", "W", "target", "ws"):
         assert fn(**{k: None}) == rz.RZ_EINVAL, k
@@ -142,6 +160,40 @@ def test_head_argument_validation(fn):
 def test_backward_needs_lse_coef_dh():
     for k in ("lse", "coef", "dh"):
         assert _backward(**{k: None}) == rz.RZ_EINVAL, k
+        assert _backward_stored(**{k: None}) == rz.RZ_EINVAL, k
+
+
+def test_logits_bytes():
+    assert rz.logits_bytes(0, 128, 1024) == 0
+    assert rz.logits_bytes(10, 0, 1024) == 0
+    assert rz.logits_bytes(10, 128, 0) == 0
+    # one chunk: the e values (rows padded for the shift table, vocabulary to
+    # whole tiles) in bf16, one max per row and vocabulary tile, one target
+    # logit per row, each region 256-byte aligned
+    b = rz.logits_bytes(300, 128, 1024)
+    assert b % 256 == 0
+    assert 300 * 1024 * 2 <= b < 2 * 300 * 1024 * 2
+    # independent of H; chunks of 32,768 rows each take the first chunk's stride
+    assert rz.logits_bytes(300, 4096, 1024) == b
+    one = rz.logits_bytes(32768, 128, 1024)
+    assert rz.logits_bytes(32769, 128, 1024) == 2 * one
+    assert rz.logits_bytes(65536, 128, 1024) == 2 * one
+    # the 1.5B-shaped head keeps about 2 bytes per logit
+    big = rz.logits_bytes(8192, 1536, 151936)
+    assert 8192 * 151936 * 2 <= big < 1.05 * 8192 * 151936 * 2
+
+
+def test_stored_logits_argument_validation():
+    for k in ("logits", "logprob"):
+        assert _logprob_store(**{k: None}) == rz.RZ_EINVAL, k
+    assert _backward_stored(logits=None) == rz.RZ_EINVAL
+    # the stored logits need 256-byte alignment and the full size
+    assert _logprob_store(logits=FAKE + 16) == rz.RZ_EINVAL
+    assert _backward_stored(logits=FAKE + 16) == rz.RZ_EINVAL
+    need = rz.logits_bytes(300, 128, 1024)
+    assert _logprob_store(lgb=need - 1) == rz.RZ_EWORKSPACE
+    assert _backward_stored(lgb=need - 1) == rz.RZ_EWORKSPACE
+    assert _logprob_store(lse=FAKE + 2) == rz.RZ_EINVAL
 
 
 def _is_loss(**kw):
@@ -323,6 +375,9 @@ def test_no_device_is_reported():
     assert _rmsnorm(rstd=None) == rz.RZ_ENODEV
     assert _logprob() == rz.RZ_ENODEV
     assert _backward() == rz.RZ_ENODEV
+    assert _logprob_store() == rz.RZ_ENODEV
+    assert _logprob_store(lse=None) == rz.RZ_ENODEV
+    assert _backward_stored() == rz.RZ_ENODEV
     assert _is_loss() == rz.RZ_ENODEV
     assert rz.lib().rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_ENODEV
     assert _step() == rz.RZ_ENODEV
