@@ -145,19 +145,41 @@ NOMINAL_SCLK_MHZ = 2400.0     # the shader clock the published MFMA peak assumes
 
 class SclkSampler:
     """Reads the GPU's current shader clock (the starred line of the amdgpu
-    driver's pp_dpm_sclk in sysfs) every 50 ms on a side thread while the
-    timed steps run.  Reports nothing when the file is absent, or when there
-    is more than one GPU and the one in use cannot be told apart."""
+    driver's pp_dpm_sclk in sysfs), and its board power where the driver's
+    hwmon files give it, every 50 ms on a side thread while the timed steps
+    run.  Reports nothing when the clock file is absent, or when there is
+    more than one GPU and the one in use cannot be told apart."""
 
     def __init__(self, interval_s: float = 0.05):
         import glob
         import threading
         files = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
         self.path = files[0] if len(files) == 1 else None
+        self.power_path = self.cap_w = None
+        if self.path:
+            hw = os.path.join(os.path.dirname(self.path), "hwmon", "hwmon*")
+            for name in ("power1_average", "power1_input"):
+                cand = sorted(glob.glob(os.path.join(hw, name)))
+                if cand:
+                    self.power_path = cand[0]
+                    break
+            cap = sorted(glob.glob(os.path.join(hw, "power1_cap")))
+            if cap:
+                self.cap_w = self._read_w(cap[0])
         self.interval = interval_s
         self.samples = []
+        self.power = []
         self._stop = threading.Event()
         self._thread = threading.Thread(target=self._run, daemon=True)
+
+    @staticmethod
+    def _read_w(path):
+        """A hwmon power file (microwatts) in watts, or None."""
+        try:
+            with open(path) as f:
+                return float(f.read().strip()) / 1e6
+        except (OSError, ValueError):
+            return None
 
     def _read(self):
         import re
@@ -176,6 +198,10 @@ class SclkSampler:
             v = self._read()
             if v is not None:
                 self.samples.append(v)
+            if self.power_path:
+                w = self._read_w(self.power_path)
+                if w is not None:
+                    self.power.append(w)
             self._stop.wait(self.interval)
 
     def __enter__(self):
@@ -192,8 +218,14 @@ class SclkSampler:
         if not self.samples:
             return None
         v = np.asarray(self.samples)
-        return {"mean_mhz": float(v.mean()), "min_mhz": float(v.min()), "max_mhz": float(v.max()),
-                "samples": int(v.size), "source": self.path}
+        out = {"mean_mhz": float(v.mean()), "min_mhz": float(v.min()), "max_mhz": float(v.max()),
+               "samples": int(v.size), "source": self.path}
+        if self.power:
+            w = np.asarray(self.power)
+            out["board_power"] = {"mean_w": float(w.mean()), "max_w": float(w.max()),
+                                  "cap_w": self.cap_w, "samples": int(w.size),
+                                  "source": self.power_path}
+        return out
 
 
 def summarize_counters(fetch_csv: str, write_csv: str, dram_csv: str = None):

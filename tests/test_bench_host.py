@@ -23,6 +23,20 @@ def test_sclk_sampler_reads_the_current_level(tmp_path):
     assert out["mean_mhz"] == 1645.0 and out["min_mhz"] == 1645.0 and out["samples"] >= 2
 
 
+def test_sclk_sampler_reads_board_power_in_watts(tmp_path):
+    f = tmp_path / "pp_dpm_sclk"
+    f.write_text("0: 500Mhz\n1: 1645Mhz *\n")
+    p = tmp_path / "power1_average"
+    p.write_text("1400000000\n")                  # microwatts
+    s = bench.SclkSampler(0.005)
+    s.path, s.power_path, s.cap_w = str(f), str(p), 1400.0
+    with s:
+        time.sleep(0.05)
+    out = s.summary()
+    assert out["board_power"]["mean_w"] == 1400.0 and out["board_power"]["cap_w"] == 1400.0
+    assert bench.SclkSampler._read_w(str(tmp_path / "absent")) is None
+
+
 def test_sclk_sampler_without_a_readout_reports_nothing(tmp_path):
     s = bench.SclkSampler(0.005)
     s.path = None
