@@ -59,6 +59,26 @@ def test_stored_pair_gives_the_recomputed_bits(rz, gpu, T, H, V):
     del logits
 
 
+def test_stored_pair_out_of_range_targets(rz, gpu):
+    """Out-of-range targets give NaN in exactly those rows, in the same bits
+    as the recomputing pair."""
+    T, H, V = 300, 128, 1000
+    say(f"stored logits with out-of-range targets T={T} H={H} V={V}")
+    xb, gb, Wb, tb, cb = _rand_case(3, T, H, V)
+    tb[[4, 77, 299]] = [V, -1, V + 12345]
+    x, g, W, t, coef = bf16(xb, gpu), bf16(gb, gpu), bf16(Wb, gpu), i32(tb, gpu), f32(cb, gpu)
+    lp, lse = rz.logprob(x, g, W, t)
+    dh = rz.backward(x, g, W, t, lse, coef)
+    slp, slse, logits = rz.logprob_store(x, g, W, t)
+    sdh = rz.backward_stored(x, g, W, t, slse, coef, logits)
+    torch.cuda.synchronize()
+    assert _same_bits(slp, lp) and _same_bits(slse, lse) and _same_bits(sdh, dh)
+    bad = np.zeros(T, bool)
+    bad[[4, 77, 299]] = True
+    assert np.isnan(host(slp)[bad]).all() and np.isfinite(host(slp)[~bad]).all()
+    assert np.isnan(host(sdh)[bad]).all() and np.isfinite(host(sdh)[~bad]).all()
+
+
 def test_stored_pair_matches_the_oracle(rz, gpu):
     T, H, V = 300, 128, 3000
     say(f"stored logits vs oracle T={T} H={H} V={V}")
