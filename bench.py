@@ -713,6 +713,11 @@ def main():
         # the same algorithmic rate against the peak at the clock the chip held
         clock["mfma_frac_algorithmic_at_this_clock"] = (
             out["mfma_frac_algorithmic"] * NOMINAL_SCLK_MHZ / clock["mean_mhz"])
+        bp = clock.get("board_power")
+        if bp:
+            # the board's energy per step at its mean power, and tokens per joule
+            bp["joules_per_step"] = bp["mean_w"] * ms_step / 1000.0
+            bp["tokens_per_joule"] = T / bp["joules_per_step"]
         out["sclk_during_timed_steps"] = clock
     if not args.no_cpu_baseline:
         log(f"cpu baseline on {args.cpu_tokens} tokens ...")
