@@ -1,9 +1,10 @@
 """Batch invariance at the 1.5B shapes (H=1536, V=151936): a fixed set of 512
 rows evaluated alone (single-row decode calls), inside batches of 7, 64, 1024
-and 65536 rows at random offsets among filler rows, and inside 2048-row
-prefill chunks.  The bits of logprob and lse must be identical across all of
-them: the kernel-mismatch term of the log-ratio decomposition is then exactly
-zero for these rows."""
+and 65536 rows at random offsets among filler rows, inside 2048-row prefill
+chunks, and through the forward that stores the logits (rz_logprob_store) in
+the 1024- and 65536-row batches.  The bits of logprob and lse must be
+identical across all of them: the kernel-mismatch term of the log-ratio
+decomposition is then exactly zero for these rows."""
 import numpy as np
 import pytest
 import torch
@@ -33,6 +34,19 @@ def test_invariance_sweep_15b(gpu):
             lse_bits[ids] = bits32(lse)[pos]
         say(f"  {label}: {len(plan)} calls")
         seen[label] = (lp_bits, lse_bits)
+    # the forward with the stored logits (rz_logprob_store), in the 1024- and
+    # 65536-row batches
+    for B in (1024, 65536):
+        lp_bits = np.zeros(n, np.uint32)
+        lse_bits = np.zeros(n, np.uint32)
+        for ids, pos, BB in sw.batches[f"batch{B}"]:
+            bx, bt = workloads.compose_batch(sw, ids, pos, BB)
+            lp, lse, lg = rz.logprob_store(bf16(bx, gpu), g, W, i32(bt, gpu), b.eps, workspace=ws)
+            lp_bits[ids] = bits32(lp)[pos]
+            lse_bits[ids] = bits32(lse)[pos]
+            del lg
+        say(f"  store{B}: {len(sw.batches[f'batch{B}'])} calls")
+        seen[f"store{B}"] = (lp_bits, lse_bits)
     ref_label = "batch1"
     for label, (a, c) in seen.items():
         np.testing.assert_array_equal(a, seen[ref_label][0], err_msg=f"logprob bits {label}")
