@@ -464,6 +464,57 @@ def shards(args, b, rz, x, g, W, tgt, lp, lse, ws):
     }), flush=True)
 
 
+def decode(args, b, rz, x, g, W, tgt, lp_full, ws):
+    """rz_logprob on small batches, the decode-style call: the first T rows
+    of the workload for T = 1 .. 2048, each call timed with HIP events on the
+    launch stream (median over the calls).  Every size runs the same 256 x
+    256 tiles as the learner step -- the price of batch invariance at small
+    T -- so the bits of each row must equal the full batch's; below 256 rows
+    a call costs about the same whatever T."""
+    import torch
+
+    dev = x.device
+    H, V = b.H, b.V
+    reps = max(args.steps, 20)
+    per = {}
+    for T in (1, 8, 64, 256, 2048):
+        lp = torch.empty(T, dtype=torch.float32, device=dev)
+        lse = torch.empty(T, dtype=torch.float32, device=dev)
+        xs, ts = x[:T], tgt[:T]
+        for _ in range(args.warmup + 1):
+            rz.logprob(xs, g, W, ts, b.eps, workspace=ws, out=lp, lse_out=lse)
+        torch.cuda.synchronize()
+        same = bool(torch.equal(lp.view(torch.int32), lp_full[:T].view(torch.int32)))
+        if not same:
+            raise SystemExit(f"decode-style call at T={T} differs from the full batch")
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(reps)]
+        for a, c in ev:
+            a.record()
+            rz.logprob(xs, g, W, ts, b.eps, workspace=ws, out=lp, lse_out=lse)
+            c.record()
+        torch.cuda.synchronize()
+        us = float(np.median([a.elapsed_time(c) for a, c in ev])) * 1000.0
+        w_gbps = 2.0 * V * H / (us * 1e-6) / 1e9
+        per[str(T)] = {"us_per_call": us, "tokens_per_s": T / (us * 1e-6),
+                       "w_read_GBps": w_gbps, "bits_equal_full_batch": same}
+        log(f"decode T={T}: {us:.1f} us per call, {T / (us * 1e-6):.0f} tokens/s, "
+            f"W read at {w_gbps:.0f} GB/s; bits equal the full batch's: {same}")
+    t1 = per["1"]
+    print(json.dumps({
+        "metric": "decode-style rz_logprob latency (one row), 1 GPU",
+        "value": t1["us_per_call"], "unit": "us", "n_gpus": 1, "steps": reps,
+        "warmup": args.warmup, "ms_per_step": t1["us_per_call"] / 1000.0,
+        "higher_is_better": False, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"{b.name}: the first T rows, H={H}, V={V}", "H": H, "V": V},
+        "per_T": per,
+        "roofline": {"kernel": "rz_logprob call", "bound": "hbm",
+                     "achieved": t1["w_read_GBps"], "peak": PEAK_HBM_BYTES / 1e9, "unit": "GB/s",
+                     "frac": t1["w_read_GBps"] * 1e9 / PEAK_HBM_BYTES, "traffic": None},
+    }), flush=True)
+
+
 def stored(args, b, rz, x, g, W, tgt, mu, ro, go, reward, ws, outs):
     """The learner head through the separate entry points with stored logits:
     rz_logprob_store, rz_is_loss, rz_backward_stored.  The whole batch's
@@ -556,6 +607,9 @@ def main():
     ap.add_argument("--shards", type=int, choices=[1, 2, 4, 8],
                     help="time the log-probabilities through this many equal shares of the "
                          "vocabulary splits and their merge instead of the learner step")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the decode-style rz_logprob call on the first 1 .. 2048 rows "
+                         "instead of the learner step")
     ap.add_argument("--stored", action="store_true",
                     help="time the separate entry points with the whole batch's logits stored "
                          "between forward and backward (rz_logprob_store, rz_is_loss, "
@@ -567,9 +621,10 @@ def main():
     args = ap.parse_args()
     if args.steps < 1 or args.warmup < 0 or args.cpu_tokens < 1:
         ap.error("--steps and --cpu-tokens must be at least 1, --warmup at least 0")
-    if sum(map(bool, (args.probe, args.shards, args.stored))) > 1 or (
-            args.grads and (args.probe or args.shards or args.stored)):
-        ap.error("--probe, --shards and --stored each time their own pass, without --grads")
+    modes = (args.probe, args.shards, args.stored, args.decode)
+    if sum(map(bool, modes)) > 1 or (args.grads and any(modes)):
+        ap.error("--probe, --shards, --stored and --decode each time their own pass, "
+                 "without --grads")
     if args.summarize_counters:
         if len(args.summarize_counters) not in (2, 3):
             ap.error("--summarize-counters takes FETCH_CSV WRITE_CSV [DRAM_CSV]")
@@ -633,6 +688,9 @@ def main():
         return
     if args.stored:
         stored(args, b, rz, x, g, W, tgt, mu, ro, go, reward, ws, outs)
+        return
+    if args.decode:
+        decode(args, b, rz, x, g, W, tgt, lp, ws)
         return
 
     def step():
