@@ -195,6 +195,8 @@ struct GemmCoreT {
   uint32_t dsh[kNA], dnxt[kNA];
   // kDeep only: LDS offsets of this stage's A and B buffers.
   uint32_t abase_ = 0, bbase_ = 0;
+  // Partial runs only: this wave's B blocks that hold a valid row.
+  int nbv = kNB;
 
   __device__ __forceinline__ void set_shift(const uint32_t* dtab, int64_t stride, int64_t a0,
                                             int64_t n_kblocks) {
@@ -313,10 +315,14 @@ struct GemmCoreT {
       fb[F][q - kNA] = *reinterpret_cast<const bf16x8*>(s + ob + (q - kNA) * kBlockBytes);
   }
 
-  template <int F>
+  // Partial: the MFMAs of B blocks j >= nbv (blocks with no valid operand-B
+  // row; nbv is uniform per wave) are skipped.  Every other output element
+  // takes the same MFMAs in the same order, so it keeps its bits.
+  template <int F, bool Partial = false>
   __device__ __forceinline__ void mfma_one(int idx) {
     const int i = idx / kNB, j = idx % kNB;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
+    if (!Partial || j < nbv)
+      acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[F][i], fb[F][j], acc[i][j], 0, 0, 0);
   }
 
   // K block of 256 (4 stages of kBK = 64) whose shifts stage kt uses.
@@ -363,7 +369,7 @@ struct GemmCoreT {
   // One full MFMA step on set F, reading step kk of stage buffer s into set
   // F^1 and issuing the loads of stage lkt (if Load; and with kDeep, A's
   // stage lkt+1 if LoadA) as the pipeline places them.
-  template <int F, bool Load, bool LoadA = false>
+  template <int F, bool Load, bool LoadA = false, bool Partial = false>
   __device__ __forceinline__ void step(const char* s, int kk, int lkt, int first_pair) {
     uint32_t oa = ANative ? aoff + uint32_t(kk * 8 * 1024) : aoff ^ uint32_t(kk << 5);
     uint32_t ob = boff ^ uint32_t(kk << 5);
@@ -373,7 +379,7 @@ struct GemmCoreT {
     }
 #pragma unroll
     for (int idx = 0; idx < kNM; ++idx) {
-      mfma_one<F>(idx);
+      mfma_one<F, Partial>(idx);
       if (idx < kNR) read_one<F ^ 1>(s, oa, ob, idx);
       if constexpr (Pipe == 0) {
         if (Load && (idx & 3) == 0 && first_pair + (idx >> 2) < kLP)
@@ -395,7 +401,7 @@ struct GemmCoreT {
   // the loads of stage kt + kStages - 1 are spread over the first steps; if
   // More, stage kt+1 is waited for and published between the halves of the
   // last step and its step-0 fragments are read during the second half.
-  template <bool Load, bool More, bool LoadA = false>
+  template <bool Load, bool More, bool LoadA = false, bool Partial = false>
   __device__ __forceinline__ void stage(int kt) {
     const char* s = kDeep ? smem : smem + (kt % kStages) * kStageBytes;
     if constexpr (kDeep) {
@@ -407,16 +413,16 @@ struct GemmCoreT {
     // wait at the end of the stage covers them too.
     if (ShiftA) load_shift(kt / kStagesPerQ + 1, dnxt);
     // steps 0 .. kSteps-2 (sets alternate 0,1,0,...), each reading the next step
-    step<0, Load, LoadA>(s, 1, lkt, 0);
+    step<0, Load, LoadA, Partial>(s, 1, lkt, 0);
     if (kSteps == 4) {
-      step<1, Load, LoadA>(s, 2, lkt, kNM / 4);
-      step<0, false>(s, 3, lkt, 0);
+      step<1, Load, LoadA, Partial>(s, 2, lkt, kNM / 4);
+      step<0, false, false, Partial>(s, 3, lkt, 0);
     }
     // last step (set 1): kSplit MFMAs, publish stage kt+1, the rest with the
     // reads of its step 0
 #pragma unroll
     for (int idx = 0; idx < kSplit; ++idx) {
-      mfma_one<1>(idx);
+      mfma_one<1, Partial>(idx);
       if (idx % kNB == kNB - 1) shift_frag<1>(idx / kNB + 1);
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -435,7 +441,7 @@ struct GemmCoreT {
       const uint32_t nb = kDeep ? boff + uint32_t(((kt + 1) % 2) * kOpStageBytes) : boff;
 #pragma unroll
       for (int idx = kSplit; idx < kNM; ++idx) {
-        mfma_one<1>(idx);
+        mfma_one<1, Partial>(idx);
         // read u goes with MFMA kSplit + u (kNM - kSplit) / kNR
 #pragma unroll
         for (int u = 0; u < kNR; ++u)
@@ -453,7 +459,7 @@ struct GemmCoreT {
     } else {
 #pragma unroll
       for (int idx = kSplit; idx < kNM; ++idx) {
-        mfma_one<1>(idx);
+        mfma_one<1, Partial>(idx);
         if (idx % kNB == kNB - 1 && idx < kNM - 1) shift_frag<1>(idx / kNB + 1);
       }
     }
@@ -499,6 +505,7 @@ struct GemmCoreT {
 
   // K must be a multiple of kBK.  Ends with no load in flight and, after the
   // trailing barrier, no LDS read outstanding, so the caller may reuse the LDS.
+  template <bool Partial = false>
   __device__ __forceinline__ void run(int K) {
     nk = K / kBK;
     if constexpr (kDeep) {
@@ -529,9 +536,9 @@ struct GemmCoreT {
       for (int q = 0; q < kNR; ++q) read_one<0>(smem, aoff, boff, q);
       shift_frag<0>(0);
       int kt = 0;
-      for (; kt + 2 < nk; ++kt) stage<true, true, true>(kt);
-      for (; kt + 1 < nk; ++kt) stage<true, true, false>(kt);
-      stage<false, false>(kt);
+      for (; kt + 2 < nk; ++kt) stage<true, true, true, Partial>(kt);
+      for (; kt + 1 < nk; ++kt) stage<true, true, false, Partial>(kt);
+      stage<false, false, false, Partial>(kt);
       barrier();
       return;
     }
@@ -546,9 +553,9 @@ struct GemmCoreT {
     for (int q = 0; q < kNR; ++q) read_one<0>(smem, aoff, boff, q);
     shift_frag<0>(0);
     int kt = 0;
-    for (; kt + kStages - 1 < nk; ++kt) stage<true, true>(kt);
-    for (; kt + 1 < nk; ++kt) stage<false, true>(kt);
-    stage<false, false>(kt);
+    for (; kt + kStages - 1 < nk; ++kt) stage<true, true, false, Partial>(kt);
+    for (; kt + 1 < nk; ++kt) stage<false, true, false, Partial>(kt);
+    stage<false, false, false, Partial>(kt);
     barrier();
   }
 };

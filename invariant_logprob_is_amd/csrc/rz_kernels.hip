@@ -233,14 +233,21 @@ constexpr int kFwdPersistentGridMax = 256;
 constexpr int kMaxDevices = 64;
 // The GEMM ring + the exchange area; a ring that fills the LDS holds the
 // exchange area in its last 2 KB, used only after the ring's final barrier.
-constexpr int kFwdLds = kFwdPipe == 2 ? 5 * kOpStageBytes : kLdsBytes + 2048;
+constexpr int fwd_lds(int pipe) { return pipe == 2 ? 5 * kOpStageBytes : kLdsBytes + 2048; }
+constexpr int kFwdLds = fwd_lds(kFwdPipe);
+// A batch of at most one token tile (the decode-style call of a few rows)
+// runs the relaunched forward with the deep ring on W (3 stages of W, 2 of
+// hhat: twice the W bytes in flight per CU) and skips the MFMAs of the
+// token blocks that hold no row.  Neither moves an MFMA of a valid row, so
+// the bits are the same as in any batch.
+constexpr int kFwdSmallPipe = 2;
 
 // Steps 1-2 of the epilogue and the partials, on the tile's accumulators.
 // Mask: the last vocabulary tile, whose rows v >= V (read as zeros) count as
 // -inf.  The masked values are formed on the fly instead of written into
 // the accumulators: in-place writes there make the compiler spill in every
 // tile's epilogue.
-template <bool Store, bool Mask, int NB>
+template <bool Store, bool Mask, int NB, int Lds = kFwdLds>
 __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* lds, int64_t tt,
                                              int64_t vt, int64_t T, int V, int64_t Vp,
                                              float* __restrict__ pm, float* __restrict__ ps,
@@ -258,7 +265,7 @@ __device__ __forceinline__ void fwd_tile_lse(const f32x16 (&acc)[4][NB], char* l
   const int wn = wave >> 1;
   const int half = lane >> 5;
   const int col = lane & 31;
-  float* xch = reinterpret_cast<float*>(lds + kFwdLds - 2048);
+  float* xch = reinterpret_cast<float*>(lds + Lds - 2048);
   // rows of this lane below V: acc_row(wm, i, r, lane) < V - v0, i.e. the
   // block offset i*32 + 8*(r/4) + r%4 (a constant of the unrolled loops)
   // below lim (the last tile only, so lim < 256)
@@ -393,7 +400,7 @@ __device__ __forceinline__ void fwd_targets(const int32_t* __restrict__ target, 
 // The epilogue of one forward tile (vocabulary tile vt, token tile tt) on its
 // accumulators: the target gather (tg from fwd_targets), then the tile's
 // partials and (Store) the stored e.
-template <bool Store, int NB>
+template <bool Store, int NB, int Lds = kFwdLds>
 __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NB], char* lds, int64_t tt,
                                              int64_t vt, const int32_t (&tgs)[NB],
                                              int64_t tgt_off, int64_t T, int V, int64_t Vp,
@@ -437,19 +444,20 @@ __device__ __forceinline__ void fwd_epilogue(const f32x16 (&acc)[4][NB], char* l
   }
 
   if (v0 + kTile > V)
-    fwd_tile_lse<Store, true>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
+    fwd_tile_lse<Store, true, NB, Lds>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
   else
-    fwd_tile_lse<Store, false>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
+    fwd_tile_lse<Store, false, NB, Lds>(acc, lds, tt, vt, T, V, Vp, pm, ps, E);
 }
 
-template <bool Store>
+template <bool Store, int Pipe = kFwdPipe>
 __global__ __launch_bounds__(64 * kFwdWaves)
 __attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
 void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
                   const int32_t* __restrict__ target, int64_t tgt_off, int64_t T, int H, int V,
                   int64_t n_vt, int64_t n_tt, int64_t Vp, float* __restrict__ pm,
                   float* __restrict__ ps, float* __restrict__ ztgt, uint16_t* __restrict__ E, int raster_group) {
-  __shared__ __attribute__((aligned(16))) char lds[kFwdLds];
+  constexpr int kLds = fwd_lds(Pipe);
+  __shared__ __attribute__((aligned(16))) char lds[kLds];
   int64_t tt, vt;
   // Vocabulary tiles are grouped (raster_group of them, chosen on the host
   // from H so that the group's W rows and the chunk's hhat fit the MALL
@@ -457,16 +465,25 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
   // (100 MB at H = 1536) stays cache-resident across the groups, where
   // re-streaming W (467 MB) from HBM for every token group would not.
   if (!tile_of(n_vt, n_tt, vt, tt, raster_group)) return;
-  using Core = GemmCoreT<false, false, kFwdWaves, 4, kFwdPipe>;
-  static_assert(Core::kLds <= kFwdLds, "LDS");
+  using Core = GemmCoreT<false, false, kFwdWaves, 4, Pipe>;
+  static_assert(Core::kLds <= kLds, "LDS");
   Core g;
   int32_t tg[Core::kNB];
   fwd_targets<Core::kNB>(target, tt, T, tg);
   g.init(W, vt * kTile, V, hhat, tt * kTile, T, H, lds);
-  g.run(H);
+  if ((tt + 1) * kTile <= T) {
+    g.run(H);
+  } else {
+    // token blocks (32 rows) of this wave below T
+    const int wn = Core::wave_n(__builtin_amdgcn_readfirstlane(int(threadIdx.x >> 6)));
+    const int64_t left = T - tt * kTile - int64_t(wn) * Core::kNB * 32;
+    g.nbv = left <= 0 ? 0 : (left >= Core::kNB * 32 ? Core::kNB : int((left + 31) / 32));
+    g.template run<true>(H);
+  }
 #pragma unroll
   for (int j = 0; j < Core::kNB; ++j) asm volatile("" : "+v"(tg[j]));
-  fwd_epilogue<Store, Core::kNB>(g.acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt, E);
+  fwd_epilogue<Store, Core::kNB, kLds>(g.acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt,
+                                       E);
 }
 
 // The same forward with one workgroup per CU: each takes the logical tile
@@ -1354,7 +1371,11 @@ static void launch_fwd_grid(const uint16_t* hhat, const uint16_t* W, const int32
                             float* pm, float* ps, float* ztgt, uint16_t* E, int* ticket,
                             hipStream_t s) {
   const uint32_t nl = raster_grid(n_vt * n_tt);
-  if (kFwdPersistent) {
+  if (n_tt == 1) {
+    hipLaunchKernelGGL((k_lmhead_fwd<Store, kFwdSmallPipe>), dim3(nl), dim3(64 * kFwdWaves), 0, s,
+                       hhat, W, target, tgt_off, T, H, V, n_vt, n_tt, vocab_pad(V), pm, ps, ztgt,
+                       E, fwd_raster_group(H));
+  } else if (kFwdPersistent) {
     hipLaunchKernelGGL(k_fill_i32, dim3(1), dim3(256), 0, s, ticket, int64_t(kFwdTickets), 0);
     const uint32_t cap = uint32_t(persistent_grid());
     const uint32_t grid = nl < cap ? nl : cap;
