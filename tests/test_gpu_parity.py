@@ -64,11 +64,13 @@ def test_tiny_logprob_matches_oracle(rz, gpu, tiny):
 
 # The contraction over the vocabulary runs Vp / 64 stages (Vp = V rounded up
 # to 64), with separate prologue and tail paths for 1, 2 and 3 stages: V = 64,
-# 128 and 129 / 192 take them.
+# 128 and 129 / 192 take them.  A batch of one token tile (T <= 256) runs the
+# forward with the deep W ring, skipping the token blocks with no row (T < 256:
+# 128 leaves two waves' blocks empty) or not (T = 256).
 @pytest.mark.parametrize("T,H,V", [(1, 64, 65), (255, 128, 1000), (257, 192, 513),
                                    (600, 64, 300), (513, 320, 256), (40, 1536, 2048),
                                    (3, 128, 64), (33, 64, 128), (300, 128, 129),
-                                   (77, 256, 192)])
+                                   (77, 256, 192), (256, 128, 1000), (128, 192, 3000)])
 def test_edge_shapes_logprob_and_backward(rz, gpu, T, H, V):
     say(f"edge shape T={T} H={H} V={V}")
     xb, gb, Wb, tb = _rand_case(T * 7 + H + V, T, H, V, wstd=0.05)

@@ -39,10 +39,11 @@ def _same_bits(a, b):
     return np.array_equal(bits32(a), bits32(b))
 
 
-# one row; several vocabulary tiles with a ragged tail; two chunks of 32,768
-# rows with a ragged second chunk; the 1.5B-shaped head over two chunks
-@pytest.mark.parametrize("T,H,V", [(1, 64, 65), (300, 128, 1024), (513, 320, 257),
-                                   (40000, 64, 1000), (33000, 1536, 151936)])
+# one row; one full token tile; several vocabulary tiles with a ragged tail;
+# two chunks of 32,768 rows with a ragged second chunk; the 1.5B-shaped head
+# over two chunks
+@pytest.mark.parametrize("T,H,V", [(1, 64, 65), (256, 128, 1000), (300, 128, 1024),
+                                   (513, 320, 257), (40000, 64, 1000), (33000, 1536, 151936)])
 def test_stored_pair_gives_the_recomputed_bits(rz, gpu, T, H, V):
     say(f"stored logits T={T} H={H} V={V} ({rz.logits_bytes(T, H, V) / 2**30:.2f} GiB)")
     xb, gb, Wb, tb, cb = _rand_case(T + H + V, T, H, V, wstd=0.05 if H < 1536 else 0.02)
