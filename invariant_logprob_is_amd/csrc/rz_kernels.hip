@@ -725,44 +725,38 @@ struct SplitPart {
 __device__ __forceinline__ SplitPart split_part(const float* __restrict__ pm,
                                                 const float* __restrict__ ps, int64_t T,
                                                 int64_t t, int64_t j0, int64_t j1) {
-  // One pass, kU tiles' (M, S) loaded at a time (the loop is latency bound
-  // at small T): the sum is kept relative to the reference of the running
-  // max and rescaled by 2^(m_old - m_new) when that rises.  Both scalings are
-  // by powers of two, so the float64 sum is the same as with the final
-  // reference applied to every term, j = j0, j0+1, ... in turn.
-  constexpr int kU = 16;
+  // Loads go out kU at a time (the loops are latency bound); the reductions
+  // still run j = j0, j0+1, ... one after another.
+  constexpr int kU = 8;
   float mx = -INFINITY;
-  float m = -INFINITY;
+  int64_t j = j0;
+  for (; j + kU <= j1; j += kU) {
+    float v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) v[u] = pm[(j + u) * T + t];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) mx = fmaxf(mx, v[u]);
+  }
+  for (; j < j1; ++j) mx = fmaxf(mx, pm[j * T + t]);
+  const float m = tile_ref(mx);
   double sum = 0.0;
-  auto add = [&](float mj, float sj) {
-    if (mj != -INFINITY) sum += ldexp(double(sj), int(fmaxf(tile_ref(mj) - m, -4096.0f)));
-  };
-  auto raise = [&](float cmx) {
-    const float nmx = fmaxf(mx, cmx);
-    const float nm = tile_ref(nmx);
-    if (nm != m) sum = ldexp(sum, int(fmaxf(m - nm, -4096.0f)));
-    mx = nmx;
-    m = nm;
-  };
-  // (the last chunk may be partial: tiles past j1 count as -inf, no term)
-  for (int64_t j = j0; j < j1; j += kU) {
+  j = j0;
+  for (; j + kU <= j1; j += kU) {
     float mj[kU], sj[kU];
 #pragma unroll
     for (int u = 0; u < kU; ++u) {
-      // a clamped address, so that every load goes out unconditionally
-      const bool in = j + u < j1;
-      const int64_t o = (in ? j + u : j1 - 1) * T + t;
-      const float a = pm[o];
-      const float b = ps[o];
-      mj[u] = in ? a : -INFINITY;
-      sj[u] = in ? b : 0.0f;
+      mj[u] = pm[(j + u) * T + t];
+      sj[u] = ps[(j + u) * T + t];
     }
-    float cmx = -INFINITY;
 #pragma unroll
-    for (int u = 0; u < kU; ++u) cmx = fmaxf(cmx, mj[u]);
-    raise(cmx);
-#pragma unroll
-    for (int u = 0; u < kU; ++u) add(mj[u], sj[u]);
+    for (int u = 0; u < kU; ++u)
+      if (mj[u] != -INFINITY)
+        sum += ldexp(double(sj[u]), int(fmaxf(tile_ref(mj[u]) - m, -4096.0f)));
+  }
+  for (; j < j1; ++j) {
+    const float mj = pm[j * T + t];
+    if (mj != -INFINITY)
+      sum += ldexp(double(ps[j * T + t]), int(fmaxf(tile_ref(mj) - m, -4096.0f)));
   }
   return {sum, m, mx};
 }
