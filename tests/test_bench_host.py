@@ -128,3 +128,11 @@ def test_summarize_counters_scales_by_the_copy_and_maps_kernels(tmp_path, monkey
     w = json.load(open(tmp_path / "profiles" / "traffic_k_dw.json"))
     assert abs(w["fetch_bytes_per_launch"] - 8e9) < 1e3
     assert abs(w["write_bytes_per_launch"] - 4e9) < 1e3
+
+
+@pytest.mark.parametrize("args", [["--decode", "--stored"], ["--decode", "--grads"],
+                                  ["--probe", "--shards", "2"]])
+def test_bench_rejects_two_modes(args):
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), *args],
+                       capture_output=True, text=True)
+    assert p.returncode == 2 and "each time their own pass" in p.stderr

@@ -39,3 +39,32 @@ def test_bench_json_line(gpu):
     assert cb["cpu_model"] and cb["affinity_cores"] >= 1
     for k, v in d["side_kernels"].items():
         assert v["achieved_GBps"] > 0 and v["ms_per_step"] > 0, k
+
+
+def _one_line(args):
+    p = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--config", "tiny",
+                        "--no-cpu-baseline", *args], capture_output=True, text=True, timeout=300)
+    assert p.returncode == 0, p.stderr[-2000:]
+    lines = [ln for ln in p.stdout.splitlines() if ln.strip()]
+    assert len(lines) == 1, p.stdout
+    return json.loads(lines[0])
+
+
+def test_bench_decode_line(gpu):
+    say("bench.py --config tiny --decode --steps 3 --warmup 1")
+    d = _one_line(["--decode", "--steps", "3", "--warmup", "1"])
+    assert d["unit"] == "us" and d["higher_is_better"] is False
+    assert d["value"] == d["per_T"]["1"]["us_per_call"] > 0
+    assert set(d["per_T"]) == {"1", "8", "64", "256"}      # the Tiny workload has ~320 rows
+    assert all(v["bits_equal_full_batch"] for v in d["per_T"].values())
+    r = d["roofline"]
+    assert r["bound"] == "hbm" and abs(r["frac"] - r["achieved"] / r["peak"]) <= 1e-9
+
+
+def test_bench_stored_line(gpu):
+    say("bench.py --config tiny --stored --steps 3 --warmup 1")
+    d = _one_line(["--stored", "--steps", "3", "--warmup", "1"])
+    assert d["bits_equal_rz_learner_step"] is True
+    T = d["config"]["T"]
+    assert abs(d["value"] - T / (d["ms_per_step"] / 1000.0)) <= 1e-6 * d["value"]
+    assert d["config"]["stored_logits_bytes"] > 0
