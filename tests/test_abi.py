@@ -404,3 +404,30 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(mod, "LIB_PATH", str(tmp_path / "nope.so"))
     with pytest.raises(RuntimeError, match="missing"):
         mod.lib()
+
+
+def test_stored_binding_checks_before_the_call():
+    # CPU tensors with a wrong dtype or shape never reach the library
+    import torch
+    x = torch.zeros(4, 64, dtype=torch.bfloat16)
+    g = torch.zeros(64, dtype=torch.bfloat16)
+    W = torch.zeros(100, 64, dtype=torch.bfloat16)
+    t = torch.zeros(4, dtype=torch.int32)
+    f = torch.zeros(4, dtype=torch.float32)
+    lg = torch.zeros(1024, dtype=torch.uint8)
+    with pytest.raises(TypeError):
+        rz.logprob_store(x.float(), g, W, t)
+    with pytest.raises(TypeError):
+        rz.logprob_store(x, g, W, t.long())
+    with pytest.raises(ValueError):
+        rz.logprob_store(x, g[:32], W, t)
+    with pytest.raises(ValueError):
+        rz.logprob_store(x, g, W, t[:3])
+    with pytest.raises(TypeError):
+        rz.backward_stored(x, g, W, t, f, f, lg.float())
+    with pytest.raises(ValueError):
+        rz.backward_stored(x, g, W, t, f[:3], f, lg)
+    with pytest.raises(ValueError):
+        rz.backward_stored(x, g, W, t, f, f[:2], lg)
+    with pytest.raises(ValueError):
+        rz.backward_stored(x, g, W, t, f, f, lg.view(32, 32))
