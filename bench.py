@@ -477,7 +477,7 @@ def decode(args, b, rz, x, g, W, tgt, lp_full, ws):
     H, V = b.H, b.V
     reps = max(args.steps, 20)
     per = {}
-    for T in (n for n in (1, 8, 64, 256, 2048) if n <= b.T):
+    for T in (n for n in (1, 8, 64, 128, 256, 2048) if n <= b.T):
         lp = torch.empty(T, dtype=torch.float32, device=dev)
         lse = torch.empty(T, dtype=torch.float32, device=dev)
         xs, ts = x[:T], tgt[:T]

@@ -486,33 +486,39 @@ void k_lmhead_fwd(const uint16_t* __restrict__ hhat, const uint16_t* __restrict_
                                        E);
 }
 
-// The forward of a batch of at most kFewRows rows (the decode-style call):
-// the token rows of the first wave column of k_lmhead_fwd's tile.  Its
-// stages hold 64 hhat rows (8 KB) instead of 256, which leaves the LDS for
-// a 4-stage ring on W: three W stages in flight instead of one.  The two
-// waves of that column (wm = 0, 1) read the same fragments and run the same
-// MFMAs in the same order on the same accumulators as in k_lmhead_fwd, skipping
-// the 32-row blocks with no row, and take the same epilogue, so every row
-// keeps its bits; the other six waves load and take part in the epilogue's
-// exchanges.
-constexpr int kFewRows = 64;
-constexpr int kFewStages = 4;
-constexpr int kFewBStage = kFewRows * kRowBytes;                       // 8 KB
-constexpr int kFewLds = kFewStages * (kOpStageBytes + kFewBStage);     // 160 KB
-static_assert(kFewLds <= 160 * 1024, "LDS");
-static_assert(kFwdWaves == 8 && kBK == 64, "the A loads are 4 per wave, the B loads 1");
+// The forward of a batch of at most R rows (R = 64 or 128, the decode-style
+// call): the token rows of the first R / 64 wave columns of k_lmhead_fwd's
+// tile.  Its stages hold R hhat rows (8 or 16 KB) instead of 256, which
+// leaves the LDS for a deeper ring on W: 4 stages at R = 64, 3 at R = 128,
+// against one W stage in flight in the 256-row tile.  The waves of those
+// columns read the same fragments and run the same MFMAs in the same order on
+// the same accumulators as in k_lmhead_fwd, skipping the 32-row blocks with
+// no row, and all waves take the same epilogue, so every row keeps its bits.
+template <int R>
+struct FewFwd {
+  static_assert(R == 64 || R == 128, "64 or 128 rows");
+  static constexpr int kBStage = R * kRowBytes;                          // 8 or 16 KB
+  static constexpr int kStages = R == 64 ? 4 : 3;
+  static constexpr int kLds = kStages * (kOpStageBytes + kBStage);        // 160 or 144 KB
+  static constexpr int kBLoads = R / kRowsPerLoad / kFwdWaves;            // 1 or 2 per wave
+  static constexpr int kLoads = 4 + kBLoads;                              // per wave and stage
+  static_assert(kLds <= 160 * 1024, "LDS");
+  static_assert(kFwdWaves == 8 && kBK == 64, "4 W loads per wave and stage");
+};
 
-// vmcnt(5 n): wait until at most n stages of this wave's loads (4 of W and
-// 1 of hhat each) are in flight.
+// vmcnt(L n): wait until at most n stages of this wave's loads (L of them
+// per stage) are in flight.
+template <int L>
 __device__ __forceinline__ void few_wait(int n) {
+  static_assert(2 * L <= 15, "vmcnt low bits");
   switch (n) {
     case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
-    case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | 5); break;
-    default: __builtin_amdgcn_s_waitcnt(0x0F70 | 10); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F70 | L); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F70 | (2 * L)); break;
   }
 }
 
-template <bool Store>
+template <bool Store, int R>
 __global__ __launch_bounds__(64 * kFwdWaves)
 __attribute__((amdgpu_waves_per_eu(kFwdWaves / 4, kFwdWaves / 4)))
 void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restrict__ W,
@@ -520,7 +526,8 @@ void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restr
                       int V, int64_t n_vt, int64_t Vp, float* __restrict__ pm,
                       float* __restrict__ ps, float* __restrict__ ztgt,
                       uint16_t* __restrict__ E, int raster_group) {
-  __shared__ __attribute__((aligned(16))) char lds[kFewLds];
+  using F = FewFwd<R>;
+  __shared__ __attribute__((aligned(16))) char lds[F::kLds];
   int64_t vt, tt;
   if (!tile_of(n_vt, 1, vt, tt, raster_group)) return;
   const int lane = threadIdx.x & 63;
@@ -532,18 +539,22 @@ void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restr
   const uint32_t ldb = uint32_t(H) * 2u;
   // load instruction q of a stage moves rows 8q .. 8q+7 into LDS bytes
   // [1024 q, 1024 q + 1024), lane l's 16 bytes at slot l % 8 of its row,
-  // holding global chunk (l % 8) ^ swz(row): W's q = 4 wave + j, hhat's q = wave
-  uint32_t va[4];
+  // holding global chunk (l % 8) ^ swz(row): W's q = 4 wave + j, hhat's
+  // q = kBLoads wave + j
+  uint32_t va[4], vb[F::kBLoads];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t row = uint32_t((wave * 4 + j) * kRowsPerLoad + lane / kChunks);
     va[j] = row * ldb + ((uint32_t(lane % kChunks) ^ swz(row)) << 4);
   }
-  const uint32_t brow = uint32_t(wave * kRowsPerLoad + lane / kChunks);
-  const uint32_t vb = brow * ldb + ((uint32_t(lane % kChunks) ^ swz(brow)) << 4);
+#pragma unroll
+  for (int j = 0; j < F::kBLoads; ++j) {
+    const uint32_t row = uint32_t((wave * F::kBLoads + j) * kRowsPerLoad + lane / kChunks);
+    vb[j] = row * ldb + ((uint32_t(lane % kChunks) ^ swz(row)) << 4);
+  }
   auto issue = [&](int st) {
-    char* sa = lds + (st % kFewStages) * kOpStageBytes;
-    char* sb = lds + kFewStages * kOpStageBytes + (st % kFewStages) * kFewBStage;
+    char* sa = lds + (st % F::kStages) * kOpStageBytes;
+    char* sb = lds + F::kStages * kOpStageBytes + (st % F::kStages) * F::kBStage;
     const int soff = st * kRowBytes;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -551,13 +562,17 @@ void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restr
       __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_void_t*)(sa + (wave * 4 + j) * 1024), 16,
                                                vo, soff, 0, 0);
     }
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t*)(sb + wave * 1024), 16, vb, soff,
-                                             0, 0);
+#pragma unroll
+    for (int j = 0; j < F::kBLoads; ++j) {
+      const uint32_t vo = vb[j];
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(
+          rb, (lds_void_t*)(sb + (wave * F::kBLoads + j) * 1024), 16, vo, soff, 0, 0);
+    }
   };
 
-  // 32-row blocks of this wave's token rows that hold a row below T (only
-  // the first wave column has token rows here)
-  const int nbv = wn != 0 ? 0 : (T >= kFewRows ? 2 : int((T + 31) / 32));
+  // 32-row blocks of this wave's token rows (wn * 64 ...) below T
+  const int64_t left = T - int64_t(wn) * 64;
+  const int nbv = (wn >= R / 64 || left <= 0) ? 0 : (left >= 64 ? 2 : int((left + 31) / 32));
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -569,19 +584,19 @@ void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restr
   fwd_targets<2>(target, tt, T, tg);
 
   const int nk = H / kBK;
-  const int pre = nk < kFewStages - 1 ? nk : kFewStages - 1;
+  const int pre = nk < F::kStages - 1 ? nk : F::kStages - 1;
   for (int st = 0; st < pre; ++st) issue(st);
-  few_wait(pre - 1);
+  few_wait<F::kLoads>(pre - 1);
   GemmCore::barrier();
   const uint32_t r32 = uint32_t(lane & 31);
   const uint32_t slot0 = (uint32_t(lane >> 5) ^ swz(r32)) << 4;
   const uint32_t aoff = uint32_t(wm * 128 + int(r32)) * kRowBytes + slot0;
-  const uint32_t boff = r32 * kRowBytes + slot0;
+  const uint32_t boff = uint32_t(wn * 64 + int(r32)) * kRowBytes + slot0;
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + kFewStages - 1 < nk) issue(kt + kFewStages - 1);
+    if (kt + F::kStages - 1 < nk) issue(kt + F::kStages - 1);
     if (nbv > 0) {
-      const char* sa = lds + (kt % kFewStages) * kOpStageBytes;
-      const char* sb = lds + kFewStages * kOpStageBytes + (kt % kFewStages) * kFewBStage;
+      const char* sa = lds + (kt % F::kStages) * kOpStageBytes;
+      const char* sb = lds + F::kStages * kOpStageBytes + (kt % F::kStages) * F::kBStage;
 #pragma unroll
       for (int kk = 0; kk < kSteps; ++kk) {
         const uint32_t oa = aoff ^ uint32_t(kk << 5);
@@ -604,15 +619,15 @@ void k_lmhead_fwd_few(const uint16_t* __restrict__ hhat, const uint16_t* __restr
     }
     if (kt + 1 < nk) {
       // stage kt+1 complete; the stages after it stay in flight
-      const int last = kt + kFewStages - 1 < nk - 1 ? kt + kFewStages - 1 : nk - 1;
-      few_wait(last - (kt + 1));
+      const int last = kt + F::kStages - 1 < nk - 1 ? kt + F::kStages - 1 : nk - 1;
+      few_wait<F::kLoads>(last - (kt + 1));
       GemmCore::barrier();
     }
   }
   GemmCore::barrier();
 #pragma unroll
   for (int j = 0; j < 2; ++j) asm volatile("" : "+v"(tg[j]));
-  fwd_epilogue<Store, 2, kFewLds>(acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt, E);
+  fwd_epilogue<Store, 2, F::kLds>(acc, lds, tt, vt, tg, tgt_off, T, V, Vp, pm, ps, ztgt, E);
 }
 
 // The same forward with one workgroup per CU: each takes the logical tile
@@ -1500,9 +1515,13 @@ static void launch_fwd_grid(const uint16_t* hhat, const uint16_t* W, const int32
                             float* pm, float* ps, float* ztgt, uint16_t* E, int* ticket,
                             hipStream_t s) {
   const uint32_t nl = raster_grid(n_vt * n_tt);
-  if (T <= kFewRows) {
-    hipLaunchKernelGGL(k_lmhead_fwd_few<Store>, dim3(nl), dim3(64 * kFwdWaves), 0, s, hhat, W,
-                       target, tgt_off, T, H, V, n_vt, vocab_pad(V), pm, ps, ztgt, E,
+  if (T <= 64) {
+    hipLaunchKernelGGL((k_lmhead_fwd_few<Store, 64>), dim3(nl), dim3(64 * kFwdWaves), 0, s, hhat,
+                       W, target, tgt_off, T, H, V, n_vt, vocab_pad(V), pm, ps, ztgt, E,
+                       fwd_raster_group(H));
+  } else if (T <= 128) {
+    hipLaunchKernelGGL((k_lmhead_fwd_few<Store, 128>), dim3(nl), dim3(64 * kFwdWaves), 0, s, hhat,
+                       W, target, tgt_off, T, H, V, n_vt, vocab_pad(V), pm, ps, ztgt, E,
                        fwd_raster_group(H));
   } else if (n_tt == 1) {
     hipLaunchKernelGGL((k_lmhead_fwd<Store, kFwdSmallPipe>), dim3(nl), dim3(64 * kFwdWaves), 0, s,

@@ -1,8 +1,9 @@
 """Batch invariance at the 1.5B shapes (H=1536, V=151936): a fixed set of 512
-rows evaluated alone (single-row decode calls), inside batches of 7, 64, 1024
-and 65536 rows at random offsets among filler rows, inside 2048-row prefill
-chunks, and through the forward that stores the logits (rz_logprob_store) in
-the 1024- and 65536-row batches.  The bits of logprob and lse must be
+rows evaluated alone (single-row decode calls), inside batches of 7, 64, 100,
+200, 1024 and 65536 rows at random offsets among filler rows (each batch size
+up to 256 rows takes one of the small-batch forwards), inside 2048-row
+prefill chunks, and through the forward that stores the logits
+(rz_logprob_store) in the 1024- and 65536-row batches.  The bits of logprob and lse must be
 identical across all of them: the kernel-mismatch term of the log-ratio
 decomposition is then exactly zero for these rows."""
 import numpy as np

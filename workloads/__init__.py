@@ -223,7 +223,8 @@ class InvarianceSweep:
     batches: dict
 
 
-def invariance_sweep(n_fixed: int = 512, sizes=(1, 7, 64, 1024, 65536), prefill_chunk: int = 2048,
+def invariance_sweep(n_fixed: int = 512, sizes=(1, 7, 64, 100, 200, 1024, 65536),
+                     prefill_chunk: int = 2048,
                      H: int = 1536, V: int = 151936, n_filler: int = 65536) -> InvarianceSweep:
     master = 2
     fx, ft = rows_only(master, _C_X, n_fixed, H, V)
