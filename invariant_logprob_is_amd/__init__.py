@@ -20,9 +20,10 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "logprob",
+    "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "rmsnorm", "logprob",
     "logprob_noalloc", "NOALLOC_SCRATCH_BYTES", "is_loss", "d3", "kl",
-    "decompose", "backward", "learner_step", "profile_enable", "profile_read", "LIB_PATH",
+    "decompose", "backward", "logits_bytes", "logprob_store", "backward_stored",
+    "learner_step", "validate_offsets", "profile_enable", "profile_read", "LIB_PATH",
     "VOCAB_SPLITS", "vocab_split_begin", "logprob_shard", "logprob_merge", "split_records",
     "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
     "RZ_EHIP", "RZ_EWORKSPACE", "SYMBOLS",
