@@ -413,6 +413,33 @@ RZ_API int rz_backward_stored(const uint16_t* x, const uint16_t* gamma, float ep
                 void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * rz_backward_grads -- rz_backward (logits NULL: the logits are recomputed)
+ * or rz_backward_stored (logits from rz_logprob_store) that also gives the
+ * gradients of the same objective with respect to the LM-head weight and
+ * the RMSNorm weight ([P2] "Alignment permits a simpler learning path": the
+ * update applies the loss gradient to all weights):
+ *   dW[v, k]  = sum_t coef_t (onehot_t - p_t)[v] hhat[t, k],
+ *   dgamma[k] = sum_t dhhat[t, k] x[t, k] r_t,
+ * with the kernels and orders of rz_learner_step's weight gradients (sorted
+ * one-hot and exact-probability terms, dW summed over 32768-row chunks in
+ * order, dgamma in float64).  coef is any per-token weight: the gradient of
+ * sum_t coef_t logprob_t, so a caller's own loss goes through it.  With the
+ * lse and coef that rz_learner_step hands out, dhidden, dW and dgamma equal
+ * that call's bit for bit.
+ *
+ * dW [V,H] fp32 (16-byte aligned) and dgamma [H] fp32 out, overwritten;
+ * workspace of at least rz_workspace_bytes_grads(T, H, V) bytes.  Errors: as
+ * rz_backward and rz_backward_stored; RZ_EINVAL without dW or dgamma.
+ */
+RZ_API int rz_backward_grads(const uint16_t* x, const uint16_t* gamma, float eps,
+                const uint16_t* W, const int32_t* target,
+                const float* lse, const float* coef,
+                int64_t T, int32_t H, int32_t V,
+                const void* logits, size_t logits_bytes,
+                float* dhidden, float* dW, float* dgamma,
+                void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * rz_learner_step -- the whole learner head for one update in one call:
  * rz_logprob, rz_is_loss, rz_d3 and the gradient to the hidden states, with
  * the log-probabilities bit-identical to rz_logprob's.

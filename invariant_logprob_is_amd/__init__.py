@@ -23,6 +23,7 @@ __all__ = [
     "RzError", "lib", "version", "workspace_bytes", "workspace_bytes_grads", "rmsnorm", "logprob",
     "logprob_noalloc", "NOALLOC_SCRATCH_BYTES", "is_loss", "d3", "kl",
     "decompose", "backward", "logits_bytes", "logprob_store", "backward_stored",
+    "backward_grads", "logprob_fn",
     "learner_step", "validate_offsets", "profile_enable", "profile_read", "LIB_PATH",
     "VOCAB_SPLITS", "vocab_split_begin", "logprob_shard", "logprob_merge", "split_records",
     "RZ_OK", "RZ_EINVAL", "RZ_EUNSUPPORTED", "RZ_ENODEV",
@@ -62,6 +63,8 @@ SYMBOLS = {
                                         _P, _SZ, _P]),
     "rz_backward_stored": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P,
                                           _SZ, _P, _P, _SZ, _P]),
+    "rz_backward_grads": (ctypes.c_int, [_P, _P, _F32, _P, _P, _P, _P, _I64, _I32, _I32, _P, _SZ,
+                                         _P, _P, _P, _P, _SZ, _P]),
     "rz_kl": (ctypes.c_int, [_P, _P, _I64, _P, _P, _SZ, _P]),
     "rz_decompose": (ctypes.c_int, [_P, _P, _P, _P, _P, _P, _F32, _P, _P, _I64, _I32, _I32, _P, _P,
                                     _P, _P, _SZ, _P]),
@@ -529,6 +532,83 @@ def backward_stored(x, gamma, W, target, lse, coef, logits, eps: float = 1e-6, *
                                   ws.numel(), _stream(dev))
     _check("rz_backward_stored", st)
     return dh
+
+
+def backward_grads(x, gamma, W, target, lse, coef, eps: float = 1e-6, *, logits=None,
+                   workspace=None, out=None):
+    """The gradient of sum_t coef_t logprob_t with respect to x, W and gamma
+    (rz_backward_grads): dhidden [T,H], dW [V,H] and dgamma [H], all fp32,
+    with the learner step's weight-gradient kernels.  `logits` may hold the
+    stored logits of logprob_store() for the same inputs (else the logits are
+    recomputed); `out` may supply preallocated dhidden, dW, dgamma."""
+    torch = _torch()
+    dev = x.device
+    _need(x, "x", torch.bfloat16, dev, 2)
+    T, H = x.shape
+    _need(gamma, "gamma", torch.bfloat16, dev, 1)
+    _need(W, "W", torch.bfloat16, dev, 2)
+    _need(target, "target", torch.int32, dev, 1)
+    _need(lse, "lse", torch.float32, dev, 1)
+    _need(coef, "coef", torch.float32, dev, 1)
+    V = W.shape[0]
+    if (gamma.shape[0] != H or W.shape[1] != H or target.shape[0] != T or lse.shape[0] != T
+            or coef.shape[0] != T):
+        raise ValueError("shape mismatch among backward arguments")
+    if logits is not None:
+        _need(logits, "logits", torch.uint8, dev, 1)
+    o = dict(out or {})
+    for k, shape in (("dhidden", (T, H)), ("dW", (V, H)), ("dgamma", (H,))):
+        if k not in o:
+            o[k] = torch.empty(shape, dtype=torch.float32, device=dev)
+        _need(o[k], k, torch.float32, dev, len(shape))
+        if tuple(o[k].shape) != shape:
+            raise ValueError(f"{k}: expected shape {shape}")
+    ws = _workspace(workspace_bytes_grads(T, H, V), dev, workspace)
+    st = lib().rz_backward_grads(x.data_ptr(), gamma.data_ptr(), float(eps), W.data_ptr(),
+                                 target.data_ptr(), lse.data_ptr(), coef.data_ptr(), T, H, V,
+                                 logits.data_ptr() if logits is not None else None,
+                                 logits.numel() if logits is not None else 0,
+                                 o["dhidden"].data_ptr(), o["dW"].data_ptr(),
+                                 o["dgamma"].data_ptr(), ws.data_ptr(), ws.numel(), _stream(dev))
+    _check("rz_backward_grads", st)
+    return o
+
+
+_logprob_fn = None
+
+
+def logprob_fn(x, gamma, W, target, eps: float = 1e-6):
+    """logprob() as a differentiable PyTorch function: the forward is
+    rz_logprob, and the backward hands the incoming gradient of the
+    log-probabilities to rz_backward as coef (only x needs a gradient) or to
+    rz_backward_grads (gamma or W need one too), so every gradient comes from
+    the library's kernels.  Autograd casts the fp32 gradients to the bf16 of
+    the inputs; rz.backward_grads gives them in fp32."""
+    global _logprob_fn
+    if _logprob_fn is None:
+        torch = _torch()
+
+        class LogprobFn(torch.autograd.Function):
+            @staticmethod
+            def forward(ctx, x, gamma, W, target, eps):
+                lp, lse = logprob(x, gamma, W, target, eps)
+                ctx.save_for_backward(x, gamma, W, target, lse)
+                ctx.eps = eps
+                return lp
+
+            @staticmethod
+            def backward(ctx, grad):
+                x, gamma, W, target, lse = ctx.saved_tensors
+                coef = grad.to(torch.float32).contiguous()
+                need_x, need_g, need_w = ctx.needs_input_grad[:3]
+                if not (need_g or need_w):
+                    return backward(x, gamma, W, target, lse, coef, ctx.eps), None, None, None, None
+                o = backward_grads(x, gamma, W, target, lse, coef, ctx.eps)
+                return (o["dhidden"] if need_x else None, o["dgamma"] if need_g else None,
+                        o["dW"] if need_w else None, None, None)
+
+        _logprob_fn = LogprobFn
+    return _logprob_fn.apply(x, gamma, W, target, float(eps))
 
 
 def learner_step(x, gamma, W, target, rollout_logprob, resp_offsets, group_offsets, reward,

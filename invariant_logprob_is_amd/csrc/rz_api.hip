@@ -141,14 +141,15 @@ int check_backward(const uint16_t* x, const uint16_t* gamma, float eps, const ui
   return RZ_OK;
 }
 
-// rz_backward, and rz_backward_stored (stored != nullptr): per chunk, the
-// forward with the e store (its (m, S, z_target) partials are recomputed
-// and left unused) or the stored chunk, the shift table from the given lse,
-// then the same contraction the learner step runs.
+// rz_backward, rz_backward_stored (stored != nullptr) and rz_backward_grads
+// (dW != nullptr): per chunk, the forward with the e store (its (m, S,
+// z_target) partials are recomputed and left unused) or the stored chunk, the
+// shift table from the given lse, then the same contractions the learner
+// step runs (with the weight gradients, dW and dgamma as well).
 hipError_t run_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
                         const int32_t* target, const float* lse, const float* coef, int64_t T,
-                        int32_t H, int32_t V, const char* stored, float* dhidden,
-                        void* workspace, hipStream_t s) {
+                        int32_t H, int32_t V, const char* stored, float* dhidden, float* dW,
+                        float* dgamma, void* workspace, hipStream_t s) {
   const WsLayout L = ws_layout(T, H, V);
   const StoredLayout SL = stored_layout(T, V);
   uint16_t* hh = at<uint16_t>(workspace, L.b_hhat);
@@ -187,8 +188,17 @@ hipError_t run_backward(const uint16_t* x, const uint16_t* gamma, float eps, con
     if (e == hipSuccess)
       e = launch_dhidden(E, D, ds, g, Wt, W, target + c0, coef + c0, tc, H, V, dhidden + c0 * H, s);
     if (e == hipSuccess) e = launch_dh_fix(rec, coef + c0, W, tc, H, dhidden + c0 * H, s);
+    if (e == hipSuccess && dW)
+      e = launch_weight_grads_chunk(E, D, ds, g, coef + c0, target + c0, hh, x + c0 * H, eps,
+                                    dhidden + c0 * H, tc, H, V, c0 / kTile, c0 == 0,
+                                    at<uint16_t>(workspace, L.g_hs), rec,
+                                    dw_exact_bufs(at<char>(workspace, L.g_dw), tc, H),
+                                    at<double>(workspace, L.g_rbuf),
+                                    at<double>(workspace, L.g_part), dW, s);
     if (e == hipSuccess) e = launch_rmsnorm_bwd(x + c0 * H, gamma, eps, tc, H, dhidden + c0 * H, s);
   }
+  if (e == hipSuccess && dW)
+    e = launch_dgamma_final(at<double>(workspace, L.g_part), ceil_div(T, kTile), H, dgamma, s);
   return e;
 }
 
@@ -421,7 +431,7 @@ int rz_backward(const uint16_t* x, const uint16_t* gamma, float eps, const uint1
   st = check_device();
   if (st != RZ_OK) return st;
   return status_of(run_backward(x, gamma, eps, W, target, lse, coef, T, H, V, nullptr, dhidden,
-                                workspace, static_cast<hipStream_t>(stream)));
+                                nullptr, nullptr, workspace, static_cast<hipStream_t>(stream)));
 }
 
 size_t rz_logits_bytes(int64_t T, int32_t H, int32_t V) {
@@ -481,7 +491,26 @@ int rz_backward_stored(const uint16_t* x, const uint16_t* gamma, float eps, cons
   st = check_device();
   if (st != RZ_OK) return st;
   return status_of(run_backward(x, gamma, eps, W, target, lse, coef, T, H, V,
-                                static_cast<const char*>(logits), dhidden, workspace,
+                                static_cast<const char*>(logits), dhidden, nullptr, nullptr,
+                                workspace, static_cast<hipStream_t>(stream)));
+}
+
+int rz_backward_grads(const uint16_t* x, const uint16_t* gamma, float eps, const uint16_t* W,
+                      const int32_t* target, const float* lse, const float* coef, int64_t T,
+                      int32_t H, int32_t V, const void* logits, size_t logits_bytes,
+                      float* dhidden, float* dW, float* dgamma, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_backward(x, gamma, eps, W, target, lse, coef, T, H, V, dhidden, workspace,
+                          workspace_bytes);
+  if (st != RZ_OK) return st;
+  if (!dW || !dgamma || !aligned16(dW) || !aligned4(dgamma)) return RZ_EINVAL;
+  if (logits && (reinterpret_cast<uintptr_t>(logits) & 255u)) return RZ_EINVAL;
+  if (workspace_bytes < ws_layout(T, H, V).grads_end) return RZ_EWORKSPACE;
+  if (logits && logits_bytes < stored_layout(T, V).total) return RZ_EWORKSPACE;
+  st = check_device();
+  if (st != RZ_OK) return st;
+  return status_of(run_backward(x, gamma, eps, W, target, lse, coef, T, H, V,
+                                static_cast<const char*>(logits), dhidden, dW, dgamma, workspace,
                                 static_cast<hipStream_t>(stream)));
 }
 

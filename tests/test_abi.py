@@ -116,6 +116,17 @@ def _backward_stored(**kw):
                                        a["lgb"], a["dh"], a["ws"], a["wsb"], a["stream"])
 
 
+def _backward_grads(**kw):
+    a = dict(x=FAKE, gamma=FAKE, eps=1e-6, W=FAKE, target=FAKE, lse=FAKE, coef=FAKE, T=300,
+             H=128, V=1024, logits=None, lgb=0, dh=FAKE, dW=FAKE, dg=FAKE, ws=FAKE, wsb=1 << 40,
+             stream=None)
+    a.update(kw)
+    return rz.lib().rz_backward_grads(a["x"], a["gamma"], a["eps"], a["W"], a["target"],
+                                      a["lse"], a["coef"], a["T"], a["H"], a["V"], a["logits"],
+                                      a["lgb"], a["dh"], a["dW"], a["dg"], a["ws"], a["wsb"],
+                                      a["stream"])
+
+
 def _rmsnorm(**kw):
     a = dict(x=FAKE, gamma=FAKE, eps=1e-6, T=300, H=128, hhat=FAKE, rstd=FAKE, stream=None)
     a.update(kw)
@@ -138,7 +149,8 @@ def test_rmsnorm_argument_validation():
     assert _rmsnorm(H=16384 + 64) == rz.RZ_EUNSUPPORTED
 
 
-@pytest.mark.parametrize("fn", [_logprob, _backward, _logprob_store, _backward_stored])
+@pytest.mark.parametrize("fn", [_logprob, _backward, _logprob_store, _backward_stored,
+                                _backward_grads])
 def test_head_argument_validation(fn):
     for k in ("x", "gamma", "W", "target", "ws"):
         assert fn(**{k: None}) == rz.RZ_EINVAL, k
@@ -194,6 +206,21 @@ def test_stored_logits_argument_validation():
     assert _logprob_store(lgb=need - 1) == rz.RZ_EWORKSPACE
     assert _backward_stored(lgb=need - 1) == rz.RZ_EWORKSPACE
     assert _logprob_store(lse=FAKE + 2) == rz.RZ_EINVAL
+
+
+def test_backward_grads_argument_validation():
+    for k in ("lse", "coef", "dh", "dW", "dg"):
+        assert _backward_grads(**{k: None}) == rz.RZ_EINVAL, k
+    assert _backward_grads(dW=FAKE + 8) == rz.RZ_EINVAL
+    assert _backward_grads(dg=FAKE + 2) == rz.RZ_EINVAL
+    # the weight gradients need the larger workspace
+    small, grads = rz.workspace_bytes(300, 128, 1024), rz.workspace_bytes_grads(300, 128, 1024)
+    assert small < grads
+    assert _backward_grads(wsb=grads - 1) == rz.RZ_EWORKSPACE
+    # stored logits: aligned, and of the full size
+    need = rz.logits_bytes(300, 128, 1024)
+    assert _backward_grads(logits=FAKE + 16, lgb=need) == rz.RZ_EINVAL
+    assert _backward_grads(logits=FAKE, lgb=need - 1) == rz.RZ_EWORKSPACE
 
 
 def _is_loss(**kw):
@@ -378,6 +405,8 @@ def test_no_device_is_reported():
     assert _logprob_store() == rz.RZ_ENODEV
     assert _logprob_store(lse=None) == rz.RZ_ENODEV
     assert _backward_stored() == rz.RZ_ENODEV
+    assert _backward_grads() == rz.RZ_ENODEV
+    assert _backward_grads(logits=FAKE, lgb=1 << 40) == rz.RZ_ENODEV
     assert _is_loss() == rz.RZ_ENODEV
     assert rz.lib().rz_d3(FAKE, FAKE, 10, FAKE, FAKE, 1 << 20, None) == rz.RZ_ENODEV
     assert _step() == rz.RZ_ENODEV
