@@ -1,5 +1,6 @@
-"""The learner step captured in a HIP graph (torch.cuda.graph around the
-C-ABI call) and replayed: the library launches only kernels on the caller's
+"""The learner step, the forward, and the stored-logits forward with the
+weight-gradient backward, captured in a HIP graph (torch.cuda.graph around
+the C-ABI calls) and replayed: the library launches only kernels on the caller's
 stream (no memset, no allocation, no host sync), so every replay must give
 the eager call's bits, with other eager work and synchronizations between the
 replays, and must follow inputs changed in place."""
@@ -112,3 +113,36 @@ def test_logprob_replays_from_a_graph(rz, gpu):
         torch.cuda.synchronize()
         assert np.array_equal(bits32(lp), bits32(ref_lp)), f"replay {rep}"
         assert np.array_equal(bits32(lse), bits32(ref_lse)), f"replay {rep}"
+
+
+def test_stored_pair_and_weight_grads_replay_from_a_graph(rz, gpu):
+    T, H, V = 5000, 128, 1000
+    say(f"graph replay of logprob_store + backward_grads T={T} H={H} V={V}")
+    xb, gb, Wb, tb, _, _, _ = _case(7, T, H, V, 2, 1)
+    x, g, W, t = bf16(xb, gpu), bf16(gb, gpu), bf16(Wb, gpu), i32(tb, gpu)
+    coef = (0.01 * torch.randn(T, device=gpu, generator=torch.Generator(gpu).manual_seed(8))
+            ).contiguous()
+    lp_e, lse_e, lg_e = rz.logprob_store(x, g, W, t)
+    ref = rz.backward_grads(x, g, W, t, lse_e, coef, logits=lg_e)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in ref.items()}
+    ref_lp = lp_e.clone()
+    ws = torch.empty(rz.workspace_bytes_grads(T, H, V), dtype=torch.uint8, device=gpu)
+    lg = torch.empty(rz.logits_bytes(T, H, V), dtype=torch.uint8, device=gpu)
+    lp = torch.empty(T, dtype=torch.float32, device=gpu)
+    lse = torch.empty(T, dtype=torch.float32, device=gpu)
+    out = {k: torch.empty_like(v) for k, v in ref.items()}
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        rz.logprob_store(x, g, W, t, logits=lg, workspace=ws, out=lp, lse_out=lse)
+        rz.backward_grads(x, g, W, t, lse, coef, logits=lg, workspace=ws, out=out)
+    for rep in range(3):
+        for v in list(out.values()) + [lp]:
+            v.fill_(float("nan"))
+        lg.fill_(0x5A)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(bits32(lp), bits32(ref_lp)), f"replay {rep}"
+        for k in ref:
+            assert np.array_equal(bits32(out[k]), bits32(ref[k])), f"replay {rep} {k}"
