@@ -460,3 +460,28 @@ def test_stored_binding_checks_before_the_call():
         rz.backward_stored(x, g, W, t, f, f[:2], lg)
     with pytest.raises(ValueError):
         rz.backward_stored(x, g, W, t, f, f, lg.view(32, 32))
+
+
+def test_a_plain_c_caller(tmp_path):
+    """include/rz.h from C: compiled with gcc, linked against the library,
+    run with the host-side checks only."""
+    import shutil
+    import subprocess
+    gcc = shutil.which("gcc")
+    if gcc is None:
+        pytest.skip("gcc not found")
+    # the plain library, and no preloaded sanitizer runtime (the sanitized
+    # run of these tests preloads one for the Python process only)
+    libdir = os.path.join(ROOT, "invariant_logprob_is_amd")
+    lib = os.path.join(libdir, "librz.so")
+    if not os.path.exists(lib):
+        pytest.skip("librz.so not built")
+    env = {k: v for k, v in os.environ.items() if k not in ("LD_PRELOAD", "ASAN_OPTIONS",
+                                                            "UBSAN_OPTIONS")}
+    exe = tmp_path / "abi_check"
+    subprocess.run([gcc, "-std=c11", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"),
+                    os.path.join(ROOT, "tests", "c", "abi_check.c"), "-o", str(exe), lib,
+                    f"-Wl,-rpath,{libdir}"], check=True, capture_output=True, text=True, env=env)
+    r = subprocess.run([str(exe)], capture_output=True, text=True, timeout=120, env=env)
+    assert r.returncode == 0, r.stdout + r.stderr
+    assert "abi_check: ok" in r.stdout
